@@ -1,0 +1,271 @@
+"""Seeded synthetic inputs for paged GQA decode attention.
+
+This module only *produces inputs*: random bf16 tensors, paged K/V pools, block
+tables, per-row page origins, positions and page maps.  It holds none of the
+attention arithmetic, so both the CPU oracle (``oracle/``) and the HIP path
+(``paged_gqa_decode_attn_amd``) can be fed from it without sharing any of the
+method's code.
+
+Generator.  The pages' GPU test for span-02 (``engine/crates/kernels/tests/gpu.rs``,
+the ``Rng`` helper) draws test data from a 64-bit LCG with multiplier
+6364136223846793005 and increment 1442695040888963407.  We keep that state
+recurrence and the draw order (K pool, then V pool, then Q), but map the state
+to ``x = (state >> 40) * 2^-23 - 1``, which lies exactly in [-1, 1): the page's
+own mapping only reaches [-1, 0).  ``x`` is exact in f32 and is turned into
+bf16 by truncation (the page's ``bf`` helper keeps the top 16 bits).
+
+Pool layout (same page, ``reference`` and ``mapped_pool`` helpers): K and V are
+separate bf16 pools ``[page][nkv][16][hd]``; token ``p`` of kv head ``kh`` for a
+row whose table starts at ``origin`` sits in physical page
+``block_table[origin + p // 16]`` (then through the page map, if any) at slot
+``p % 16``.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import Optional
+
+import numpy as np
+
+PAGE = 16  # tokens per page (the pool layout fixes it)
+BF16_QNAN = 0x7FC0  # bf16 quiet NaN the page fills its null page with
+
+_MUL = 6364136223846793005
+_INC = 1442695040888963407
+_MASK = (1 << 64) - 1
+
+_tables: dict = {}
+
+
+def _jump_tables(n: int):
+    """Affine maps s -> A[k]*s + C[k] (mod 2^64) for k = 1..n LCG steps."""
+    best = _tables.get("t")
+    if best is not None and len(best[0]) >= n:
+        return best[0][:n], best[1][:n]
+    a = np.array([_MUL], dtype=np.uint64)
+    c = np.array([_INC], dtype=np.uint64)
+    while len(a) < n:
+        an, cn = np.uint64(int(a[-1])), np.uint64(int(c[-1]))
+        # step k + m = (step k) o (step m):  A_{k+m} = A_k A_m,  C_{k+m} = A_k C_m + C_k
+        a, c = np.concatenate([a, a * an]), np.concatenate([c, a * cn + c])
+    _tables["t"] = (a, c)
+    return a[:n], c[:n]
+
+
+class Lcg:
+    """64-bit LCG with the span-02 test's constants; vectorised by jump-ahead."""
+
+    BLOCK = 1 << 22
+
+    def __init__(self, seed: int):
+        self.state = seed & _MASK
+
+    def step(self) -> int:
+        self.state = (self.state * _MUL + _INC) & _MASK
+        return self.state
+
+    def u32(self) -> int:
+        """High 32 bits of the state after one step (integer draws)."""
+        return self.step() >> 32
+
+    def states(self, n: int) -> np.ndarray:
+        """The next ``n`` states, as uint64, advancing the generator by ``n``."""
+        out = np.empty(n, dtype=np.uint64)
+        done = 0
+        while done < n:
+            m = min(self.BLOCK, n - done)
+            a, c = _jump_tables(m)
+            blk = a * np.uint64(self.state) + c
+            out[done:done + m] = blk
+            self.state = int(blk[-1])
+            done += m
+        return out
+
+    def uniform_bf16(self, n: int, scale: float = 1.0) -> np.ndarray:
+        """``n`` bf16 bit patterns of ``scale * x``, x uniform in [-1, 1)."""
+        out = np.empty(n, dtype=np.uint16)
+        done = 0
+        sc = np.float32(scale)
+        while done < n:
+            m = min(self.BLOCK, n - done)
+            a, c = _jump_tables(m)
+            blk = a * np.uint64(self.state) + c
+            self.state = int(blk[-1])
+            x = (blk >> np.uint64(40)).astype(np.float32) * np.float32(2.0 ** -23) - np.float32(1.0)
+            if scale != 1.0:
+                x = x * sc
+            out[done:done + m] = (x.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+            done += m
+        return out
+
+
+@dataclasses.dataclass
+class Workload:
+    """One decode call's inputs, all host numpy arrays (bf16 as uint16 bits)."""
+
+    name: str
+    rows: int
+    nh: int
+    nkv: int
+    hd: int
+    window: int
+    q: np.ndarray  # uint16 [rows, nh, hd]
+    k_pool: np.ndarray  # uint16 [npages, nkv, 16, hd]
+    v_pool: np.ndarray  # uint16 [npages, nkv, 16, hd]
+    block_table: np.ndarray  # int32
+    page_origin: np.ndarray  # int32 [rows]
+    qpos: np.ndarray  # int32 [rows]
+    kv_last: np.ndarray  # int32 [rows]
+    page_map: Optional[np.ndarray] = None  # int32, indexed by block-table entry
+    note: str = ""
+
+    @property
+    def npages(self) -> int:
+        return int(self.k_pool.shape[0])
+
+    def replace(self, **kw) -> "Workload":
+        return dataclasses.replace(self, **kw)
+
+
+def _draw_pools(rng: Lcg, npages: int, nkv: int, hd: int, k_scale: float = 1.0):
+    n = npages * nkv * PAGE * hd
+    k = rng.uniform_bf16(n, k_scale).reshape(npages, nkv, PAGE, hd)
+    v = rng.uniform_bf16(n).reshape(npages, nkv, PAGE, hd)
+    return k, v
+
+
+def single_sequence(name: str, ctx: int, rows: int, nh: int, nkv: int, hd: int,
+                    window: int, seed: Optional[int] = None, k_scale: float = 1.0) -> Workload:
+    """The span-02 ``run()`` fixture: rows at positions ctx-rows..ctx-1 of one
+    sequence, ``ceil(ctx/16) + 1`` pool pages (one spare), identity block table,
+    origin 0.  Seed defaults to ``12345 + hd`` as on the page."""
+    rng = Lcg(12345 + hd if seed is None else seed)
+    npg = (ctx + PAGE - 1) // PAGE + 1
+    k, v = _draw_pools(rng, npg, nkv, hd, k_scale)
+    q = rng.uniform_bf16(rows * nh * hd).reshape(rows, nh, hd)
+    bt = np.arange((ctx + PAGE - 1) // PAGE, dtype=np.int32)
+    qpos = np.arange(ctx - rows, ctx, dtype=np.int32)
+    return Workload(name, rows, nh, nkv, hd, window, q, k, v, bt,
+                    np.zeros(rows, np.int32), qpos, qpos.copy())
+
+
+def first_live_page(w: Workload) -> int:
+    """Lowest logical page any row can see (row 0's window start // 16), as the
+    page's page-map fixture computes it; 0 for global (window 0) layers."""
+    if w.window <= 0:
+        return 0
+    q0 = int(w.qpos[0])
+    lo_row = q0 + 1 - min(w.window, q0 + 1)
+    return lo_row // PAGE
+
+
+def mapped_pool(k: np.ndarray, v: np.ndarray, first_live: int):
+    """Permuted copy of a ``[npg][nkv][16][hd]`` pool behind a page map.
+
+    The result has ``npg + 1`` pages.  Physical page 0 is a null page filled with
+    bf16 NaN; logical page ``p >= first_live`` lives at physical page ``npg - p``;
+    the map sends logical pages below ``first_live`` to the null page."""
+    npg = k.shape[0]
+    mk = np.full((npg + 1,) + k.shape[1:], BF16_QNAN, dtype=np.uint16)
+    mv = np.full((npg + 1,) + v.shape[1:], BF16_QNAN, dtype=np.uint16)
+    pmap = np.zeros(npg, dtype=np.int32)
+    for p in range(first_live, npg):
+        s = npg - p
+        pmap[p] = s
+        mk[s] = k[p]
+        mv[s] = v[p]
+    return mk, mv, pmap
+
+
+def with_page_map(w: Workload, first_live: Optional[int] = None) -> Workload:
+    """Same logical K/V as ``w`` (identity table) in a permuted pool + page map."""
+    fl = first_live_page(w) if first_live is None else first_live
+    mk, mv, pmap = mapped_pool(w.k_pool, w.v_pool, fl)
+    return w.replace(name=w.name + "+pagemap", k_pool=mk, v_pool=mv, page_map=pmap,
+                     note=f"permuted pool, first_live={fl}, null page 0 = NaN")
+
+
+def batched(name: str = "C4", nseq: int = 64, lmin: int = 512, lmax: int = 16384,
+            nh: int = 32, nkv: int = 8, hd: int = 128, window: int = 0,
+            len_seed: int = 777, data_seed: int = 12345 + 128, pad: int = 16,
+            nan_tail: bool = False) -> Workload:
+    """Batched decode: ``nseq`` sequences, one query row each, at their last position.
+
+    Lengths ``L_s = lmin + u32 % (lmax - lmin + 1)`` from ``Lcg(len_seed)``; each
+    sequence holds ``ceil(L_s/16)`` pages.  Physical pages ``1..N`` are shuffled
+    (Fisher-Yates, same generator) and dealt to the sequences in order, so each
+    sequence is a random permutation inside one shared pool.  Physical page 0 is
+    a NaN null page.  The block table starts with ``pad`` entries pointing at the
+    null page, then every sequence's pages; row ``s`` has origin
+    ``pad + sum(P_<s)`` (distinct, non-zero; reading a pad entry returns NaN).
+    K, V (physical pages 1..N in order) and Q come from ``Lcg(data_seed)``.  With
+    ``nan_tail`` the unused slots of each sequence's last page are NaN too."""
+    r = Lcg(len_seed)
+    lens = [lmin + r.u32() % (lmax - lmin + 1) for _ in range(nseq)]
+    pages = [(L + PAGE - 1) // PAGE for L in lens]
+    total = sum(pages)
+    perm = list(range(1, total + 1))
+    for i in range(total - 1, 0, -1):
+        j = r.u32() % (i + 1)
+        perm[i], perm[j] = perm[j], perm[i]
+    bt = np.array([0] * pad + perm, dtype=np.int32)
+    origins = np.cumsum([0] + pages[:-1]).astype(np.int64) + pad
+    rng = Lcg(data_seed)
+    npages = total + 1
+    k = np.empty((npages, nkv, PAGE, hd), dtype=np.uint16)
+    v = np.empty((npages, nkv, PAGE, hd), dtype=np.uint16)
+    k[0] = BF16_QNAN
+    v[0] = BF16_QNAN
+    n = total * nkv * PAGE * hd
+    k[1:] = rng.uniform_bf16(n).reshape(total, nkv, PAGE, hd)
+    v[1:] = rng.uniform_bf16(n).reshape(total, nkv, PAGE, hd)
+    q = rng.uniform_bf16(nseq * nh * hd).reshape(nseq, nh, hd)
+    if nan_tail:
+        for s, L in enumerate(lens):
+            used = L % PAGE
+            if used:
+                phys = bt[origins[s] + pages[s] - 1]
+                k[phys, :, used:, :] = BF16_QNAN
+                v[phys, :, used:, :] = BF16_QNAN
+    qpos = np.array([L - 1 for L in lens], dtype=np.int32)
+    return Workload(name, nseq, nh, nkv, hd, window, q, k, v, bt,
+                    origins.astype(np.int32), qpos, qpos.copy(),
+                    note=f"{nseq} seqs, lengths U[{lmin},{lmax}] seed {len_seed}")
+
+
+# ---------------------------------------------------------------------------
+# The named workloads.  C1..C5 are the decode shapes this project is measured
+# on; PA and PB are the two shapes the span-02 test runs
+# (``attention_matches_reference``).
+# ---------------------------------------------------------------------------
+
+def make(name: str) -> Workload:
+    n = name.upper()
+    if n == "C1":
+        return single_sequence("C1", ctx=64, rows=1, nh=4, nkv=1, hd=64, window=0)
+    if n == "C2":
+        return single_sequence("C2", ctx=4096, rows=4, nh=16, nkv=8, hd=256, window=1024)
+    if n == "C3":
+        return single_sequence("C3", ctx=32768, rows=1, nh=16, nkv=2, hd=512, window=0)
+    if n == "C4":
+        return batched("C4")
+    if n == "C4NAN":
+        return batched("C4nan", nan_tail=True)
+    if n in ("C5", "C5W0"):
+        return single_sequence("C5w0", ctx=131072, rows=8, nh=8, nkv=1, hd=256, window=0, k_scale=8.0)
+    if n == "C5W4096":
+        return single_sequence("C5w4096", ctx=131072, rows=8, nh=8, nkv=1, hd=256, window=4096,
+                               k_scale=8.0)
+    if n == "PA":
+        return single_sequence("PA", ctx=1500, rows=5, nh=16, nkv=8, hd=256, window=1024)
+    if n == "PB":
+        return single_sequence("PB", ctx=700, rows=1, nh=16, nkv=2, hd=512, window=0)
+    raise KeyError(name)
+
+
+NAMES = ("C1", "C2", "C3", "C4", "C4nan", "C5w0", "C5w4096", "PA", "PB")
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """Widen bf16 bit patterns to float32 (exact)."""
+    return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
