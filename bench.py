@@ -1,0 +1,231 @@
+"""Benchmark: paged GQA decode attention on one MI355X.
+
+One step = one ``pgqa_attn_decode`` call (split-partial kernel plus its merge)
+over one batch of synthetic, seeded inputs already resident in HBM.  The
+default workload is the batched decode: 64 sequences x 1 query row, lengths
+uniform in [512, 16384], nh=32, nkv=8, hd=128, global causal (about 2.2 GB of
+K/V).  Prints one JSON line on stdout; extra per-configuration lines go to
+stderr with --all.
+
+Metric: effective KV bandwidth = algorithmic K/V bytes / time, where every
+visible key is counted once per (sequence, kv head): |union of the rows'
+visible spans| * nkv * hd * 2 (K and V) * 2 bytes.  Rows/s is reported beside it.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import workloads  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def visible_union_tokens(w) -> int:
+    """Keys visible to at least one row, counted once per sequence (rows that
+    share a page origin share a sequence)."""
+    spans = {}
+    for t in range(w.rows):
+        q = int(w.qpos[t])
+        lo = max(0, q + 1 - w.window) if w.window > 0 else 0
+        hi = int(w.kv_last[t])
+        if hi >= lo:
+            spans.setdefault(int(w.page_origin[t]), []).append((lo, hi))
+    total = 0
+    for iv in spans.values():
+        iv.sort()
+        cur_lo, cur_hi = iv[0]
+        for lo, hi in iv[1:]:
+            if lo > cur_hi + 1:
+                total += cur_hi - cur_lo + 1
+                cur_lo, cur_hi = lo, hi
+            else:
+                cur_hi = max(cur_hi, hi)
+        total += cur_hi - cur_lo + 1
+    return total
+
+
+def kv_bytes(w) -> int:
+    return visible_union_tokens(w) * w.nkv * w.hd * 2 * 2
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    with open(os.path.join(ROOT, "paged_gqa_decode_attn_amd", "csrc", "pgqa.hip"), "rb") as f:
+        h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def committed_traffic(config: str):
+    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    try:
+        with open(path) as f:
+            rec = json.load(f).get(config)
+    except (OSError, ValueError):
+        return None
+    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def run_config(name, steps, warmup, mode, splits_override, flush):
+    import torch
+
+    import paged_gqa_decode_attn_amd as pg
+    from tests.gpu_util import DeviceWorkload  # upload helper only
+
+    t0 = time.perf_counter()
+    w = workloads.make(name)
+    log(f"[bench] {name}: generated in {time.perf_counter() - t0:.1f}s "
+        f"(rows={w.rows} nh={w.nh} nkv={w.nkv} hd={w.hd} window={w.window} pages={w.npages})")
+    dw = DeviceWorkload(w)
+    rps = 1 if name.upper().startswith("C4") else w.rows
+    splits = splits_override or dw.heuristic_splits(rows_per_seq=rps)
+    counters = torch.zeros(pg.counter_capacity(), dtype=torch.int32, device="cuda") if mode == "fused" else None
+    out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
+    part = torch.empty(max(1, pg.decode_part_bytes(w.rows, w.nh, splits, w.hd)), dtype=torch.uint8, device="cuda")
+    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    stream = torch.cuda.current_stream()
+
+    def step():
+        dw.run(splits, counters=counters, out=out, part=part, sync=False)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    torch.cuda.synchronize()
+    wall0 = time.perf_counter()
+    for i in range(steps):
+        if scratch is not None:
+            scratch.add_(1)  # evicts L2 and the Infinity Cache between steps
+        ev[i][0].record(stream)
+        step()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - wall0
+    per = np.array([a.elapsed_time(b) for a, b in ev])  # ms, per launch
+    b = kv_bytes(w)
+    res = dict(name=name, splits=splits, mode=mode, kv_bytes=b, rows=w.rows,
+               kernel_ms_mean=float(per.mean()), kernel_ms_median=float(np.median(per)),
+               kernel_ms_min=float(per.min()), wall_ms_per_step=wall * 1e3 / steps)
+    res["eff_gbs"] = b / (res["kernel_ms_mean"] * 1e-3) / 1e9
+    res["eff_gbs_median"] = b / (res["kernel_ms_median"] * 1e-3) / 1e9
+    res["rows_per_s"] = w.rows / (res["kernel_ms_mean"] * 1e-3)
+    res["_w"], res["_out"] = w, out
+    return res
+
+
+def cpu_baseline(w, budget_s=12.0):
+    """The oracle, as it stands, on a bounded sample of the workload's rows."""
+    import oracle
+
+    threads = os.cpu_count() or 1
+    rows = []
+    order = np.arange(w.rows)
+    # grow the sample until it costs about budget_s
+    n = 1
+    elapsed = 0.0
+    out = None
+    while True:
+        sub = oracle.rows_subset(w, order[:n])
+        t0 = time.perf_counter()
+        out = oracle.decode(sub, threads=threads)
+        elapsed = time.perf_counter() - t0
+        if elapsed > budget_s / 4 or n >= w.rows:
+            break
+        n = min(w.rows, n * 4)
+    rows = order[:n]
+    b = kv_bytes(oracle.rows_subset(w, rows))
+    return dict(value=b / elapsed / 1e9, unit="GB/s", cores=threads, kind="oracle",
+                sample=f"{n} of {w.rows} rows ({b / 1e9:.3f} GB of K/V), {elapsed:.2f}s, "
+                       f"{n / elapsed:.2f} rows/s"), rows, out
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--config", default="C4")
+    ap.add_argument("--mode", choices=["fused", "separate"], default="fused")
+    ap.add_argument("--splits", type=int, default=0)
+    ap.add_argument("--flush", action="store_true", help="evict caches between steps")
+    ap.add_argument("--all", action="store_true", help="also time the other configs (stderr)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+
+    assert torch.cuda.is_available(), "bench needs a GPU"
+    res = run_config(args.config, args.steps, args.warmup, args.mode, args.splits, args.flush)
+    w = res.pop("_w")
+    out = res.pop("_out")
+    log("[bench] " + json.dumps({k: v for k, v in res.items()}))
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        import oracle
+
+        cpu, rows, ref = cpu_baseline(w)
+        gpu_rows = out.cpu().numpy().view(np.uint16)[rows]
+        res["rel_rms_sample"] = oracle.rel_rms(gpu_rows, ref)
+        log(f"[bench] cpu baseline {cpu}; rel_rms on sample {res['rel_rms_sample']:.3e}")
+
+    if args.all:
+        for name in ("C1", "C2", "C3", "C5W0", "C5W4096", "PA", "PB"):
+            r = run_config(name, 20, 3, args.mode, 0, True)
+            r.pop("_w"), r.pop("_out")
+            log("[bench] " + json.dumps(r))
+            torch.cuda.empty_cache()
+
+    ms = res["kernel_ms_mean"]
+    traffic = committed_traffic(args.config)
+    line = {
+        "metric": "paged GQA decode attention: effective KV HBM GB/s and query rows/sec",
+        "value": round(res["eff_gbs"], 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["wall_ms_per_step"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "rows_per_s": round(res["rows_per_s"], 1),
+        "config": {"workload": args.config, "rows": w.rows, "nh": w.nh, "nkv": w.nkv, "hd": w.hd,
+                   "window": w.window, "splits": res["splits"], "merge": args.mode,
+                   "kv_bytes": res["kv_bytes"], "parallelism": "single-gpu"},
+        "roofline": {"bound": "hbm", "achieved": round(res["eff_gbs"], 2), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(res["eff_gbs"] / HBM_PEAK_GBS, 4),
+                     "traffic": traffic, "kernel_ms": round(ms, 5)},
+        "cpu_baseline": cpu,
+    }
+    if "rel_rms_sample" in res:
+        line["rel_rms_sample"] = res["rel_rms_sample"]
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

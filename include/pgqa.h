@@ -1,0 +1,137 @@
+/*
+ * pgqa — paged grouped-query decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * C ABI of libpgqa.so.  Plain pointers and sizes only; no framework types.
+ *
+ * Source of the contract: the span-02 GPU kernel test page
+ * (respanai/span-02, engine/crates/kernels/tests/gpu.rs), function `run()`:
+ * its `attn::choose_splits`, `attn::decode_part_bytes` and `attn::attn_decode`
+ * calls fix the argument list and order, the pool layout, the 4096-entry
+ * counter buffer, the "null counters selects a separate combine kernel" rule
+ * and the page-map argument.  The page does not give the split rule, the
+ * partial-buffer size formula or the second position array's meaning; the
+ * readings taken here are stated at each declaration.
+ *
+ * Conventions for every entry point:
+ *   - Device pointers point to memory of the current HIP device, owned by the
+ *     caller.  The library allocates nothing and never synchronises: work is
+ *     enqueued on `stream` (a hipStream_t; NULL = the null stream) and the call
+ *     returns.
+ *   - bf16 tensors are arrays of uint16_t bit patterns.
+ *   - A negative return code means the call was refused *before* anything was
+ *     enqueued (buffers untouched); pgqa_last_error() then describes why.
+ */
+#ifndef PGQA_H
+#define PGQA_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define PGQA_OK 0
+#define PGQA_EINVAL (-1)  /* bad pointer, shape, window or split count           */
+#define PGQA_ECAP (-2)    /* more merge units than the counter buffer holds       */
+#define PGQA_ELAUNCH (-3) /* the HIP runtime reported an error at launch          */
+
+/* Tokens per KV page; the pool layout fixes it. */
+#define PGQA_PAGE 16
+/* Largest split count attn_decode accepts. */
+#define PGQA_MAX_SPLITS 256
+
+/*
+ * Number of KV splits for a decode call (span-02 test page, `run()`: the
+ * `choose_splits` call, made with the visible span, the row count, nkv and the
+ * row count again).
+ *   kv_span      - keys a row can see: min(ctx, window) for a sliding layer,
+ *                  ctx otherwise (longest sequence for a batch).
+ *   rows         - query rows in the call.
+ *   nkv          - kv heads.
+ *   rows_per_seq - query rows that share one sequence (one block-table span);
+ *                  the page passes `rows` (all rows on one sequence).  Values
+ *                  < 1 or > rows are read as rows.
+ * Returns a split count in [1, PGQA_MAX_SPLITS].  It only affects speed: every
+ * count in that range gives a correct result.  Never fails.
+ */
+int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t rows_per_seq);
+
+/*
+ * Bytes of the partial-result buffer attn_decode needs for `splits` splits
+ * (span-02 test page, `run()`: the `decode_part_bytes` call).  Formula (ours):
+ * rows * nh * splits * (hd + 2) * 4 -- an f32 unnormalised output row plus the
+ * running max and sum for every (row, query head, split).  Returns 0 for
+ * non-positive arguments.  With splits == 1 the buffer is not used.
+ */
+uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_t hd);
+
+/* Entries of int32 the merge-counter buffer must hold: 4096 (span-02 test page,
+ * `run()`, the zeroed `cnt` buffer of 4096 * 4 bytes). */
+int32_t pgqa_counter_capacity(void);
+
+/*
+ * Paged GQA decode attention (span-02 test page, `run()`: the `attn_decode`
+ * calls, and the `reference` function for what is computed).
+ *
+ * For every query row t and query head h, with kv head kh = h / (nh / nkv):
+ *   visible keys p:  lo_t <= p <= kv_last[t],
+ *                    lo_t = max(0, qpos[t] + 1 - window) if window > 0, else 0
+ *   key p's K/V row: pool[phys][kh][p % 16][0..hd), where
+ *                    phys = block_table[page_origin[t] + p / 16],
+ *                    then phys = page_map[phys] if page_map != NULL
+ *   out[t][h][:] = sum_p softmax_p(q[t][h] . K_p) * V_p   (scale 1.0)
+ * rounded to bf16 (nearest even); 0 if no key is visible.
+ *
+ * Arguments (order as on the page, with the stream last):
+ *   out         bf16 [rows][nh][hd]                      (written)
+ *   part        partial buffer, >= pgqa_decode_part_bytes(rows, nh, splits, hd)
+ *               bytes, 4-byte aligned; may be NULL when splits == 1.  Contents
+ *               are undefined after the call.
+ *   q           bf16 [rows][nh][hd]
+ *   k_pool      bf16 [npages][nkv][16][hd]
+ *   v_pool      bf16 [npages][nkv][16][hd]
+ *   block_table int32 page ids; row t's table starts at entry page_origin[t]
+ *   page_origin int32 [rows]
+ *   qpos        int32 [rows] query positions (the window is anchored here)
+ *   kv_last     int32 [rows] last visible key per row.  The page passes the
+ *               query positions again here (causal decode); only
+ *               kv_last == qpos is checked against its reference.
+ *   rows, nh, nkv, hd  shapes: nh % nkv == 0, hd in {64, 128, 256, 512}
+ *   window      0 = global causal, > 0 = sliding window of that many keys
+ *   splits      1..PGQA_MAX_SPLITS, normally from pgqa_choose_splits
+ *   counters    NULL: a separate combine kernel merges the splits.  Non-NULL:
+ *               int32 [pgqa_counter_capacity()], all zero before the first
+ *               call; the last workgroup of each merge unit merges and resets
+ *               its counter, so the buffer is all zero again when the call
+ *               completes and can be reused without clearing.
+ *   page_map    NULL, or int32 indexed by block-table entries (see above)
+ *   stream      hipStream_t
+ *
+ * The caller guarantees: every block-table entry, page-map entry and pool page
+ * reached for a visible key is in range (pages that hold no visible key of any
+ * row sharing the origin are never read, so they may point anywhere -- e.g. at
+ * a NaN-filled null page); the K/V rows of visible keys are finite.
+ * Rows that share an origin and sit next to each other are processed together
+ * and read each KV page once.  Bitwise properties: the result does not depend
+ * on `counters` (fused merge == separate combine), nor on where pages live in
+ * the pool (identity table == permuted pool behind a page map).
+ * `out` must not alias any input or `part`.  Calls that share `part` or
+ * `counters` must not run concurrently.
+ * Returns PGQA_OK, PGQA_EINVAL, PGQA_ECAP (counters given and
+ * rows * nkv * ceil(nh / nkv / 16) > pgqa_counter_capacity()) or PGQA_ELAUNCH.
+ */
+int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool,
+                     const void *v_pool, const int32_t *block_table,
+                     const int32_t *page_origin, const int32_t *qpos,
+                     const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv,
+                     int64_t hd, int64_t window, int64_t splits, int32_t *counters,
+                     const int32_t *page_map, void *stream);
+
+/* Message for the last non-zero return on this thread ("" if none). */
+const char *pgqa_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PGQA_H */

@@ -1,0 +1,134 @@
+"""Paged GQA decode attention on AMD MI355X (gfx950): Python binding.
+
+A thin ctypes layer over ``libpgqa.so`` (declared in ``include/pgqa.h``).  It
+only marshals arguments -- torch tensors (or raw device addresses) to pointers,
+the current torch stream to a ``hipStream_t`` -- and raises on a non-zero
+return.  Every step of the computation runs in the HIP kernels; there is no
+CPU or framework fallback, and a missing library is an error.
+
+Entry points (same names and argument order as the C ABI, after the span-02
+GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
+``counter_capacity``, ``attn_decode``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libpgqa.so")
+
+PAGE = 16
+MAX_SPLITS = 256
+OK, EINVAL, ECAP, ELAUNCH = 0, -1, -2, -3
+
+
+class PgqaError(RuntimeError):
+    def __init__(self, code: int, msg: str):
+        super().__init__(f"pgqa error {code}: {msg}")
+        self.code = code
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded C library; raises if it has not been built."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise PgqaError(EINVAL, f"{LIB_PATH} is not built; run __graft_entry__.build() "
+                                    "or python -m paged_gqa_decode_attn_amd._build")
+        h = ctypes.CDLL(LIB_PATH)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        h.pgqa_choose_splits.restype = ctypes.c_int32
+        h.pgqa_choose_splits.argtypes = [i64, i64, i64, i64]
+        h.pgqa_decode_part_bytes.restype = ctypes.c_uint64
+        h.pgqa_decode_part_bytes.argtypes = [i64, i64, i64, i64]
+        h.pgqa_counter_capacity.restype = ctypes.c_int32
+        h.pgqa_counter_capacity.argtypes = []
+        h.pgqa_last_error.restype = ctypes.c_char_p
+        h.pgqa_last_error.argtypes = []
+        h.pgqa_attn_decode.restype = ctypes.c_int
+        h.pgqa_attn_decode.argtypes = [p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
+                                       p, p, p]
+        _lib = h
+    return _lib
+
+
+def choose_splits(kv_span: int, rows: int, nkv: int, rows_per_seq: int) -> int:
+    return int(lib().pgqa_choose_splits(kv_span, rows, nkv, rows_per_seq))
+
+
+def decode_part_bytes(rows: int, nh: int, splits: int, hd: int) -> int:
+    return int(lib().pgqa_decode_part_bytes(rows, nh, splits, hd))
+
+
+def counter_capacity() -> int:
+    return int(lib().pgqa_counter_capacity())
+
+
+def last_error() -> str:
+    return lib().pgqa_last_error().decode()
+
+
+def _addr(x, name, dtypes=None, min_numel=None):
+    """Device address of a tensor (checked) or of a raw integer address."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if not getattr(x, "is_cuda", False):
+        raise PgqaError(EINVAL, f"{name} must be a device tensor")
+    if not x.is_contiguous():
+        raise PgqaError(EINVAL, f"{name} must be contiguous")
+    if dtypes is not None and x.dtype not in dtypes:
+        raise PgqaError(EINVAL, f"{name} has dtype {x.dtype}")
+    if min_numel is not None and x.numel() < min_numel:
+        raise PgqaError(EINVAL, f"{name} has {x.numel()} elements, needs {min_numel}")
+    return x.data_ptr()
+
+
+def attn_decode(out, part, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last,
+                rows: int, nh: int, nkv: int, hd: int, window: int, splits: int,
+                counters=None, page_map=None, stream=None) -> None:
+    """Enqueue one decode call (see ``pgqa_attn_decode`` in include/pgqa.h).
+
+    Tensors: bf16 (or 16-bit integer views of bf16) ``out``/``q`` [rows][nh][hd],
+    pools [npages][nkv][16][hd]; int32 ``block_table``, ``page_origin``,
+    ``qpos``, ``kv_last``, ``counters``, ``page_map``; ``part`` any dtype with
+    at least ``decode_part_bytes`` bytes.  ``stream`` defaults to torch's current
+    stream on the tensors' device."""
+    import torch
+
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    i32 = (torch.int32,)
+    n_out = rows * nh * hd
+    args = [
+        _addr(out, "out", b16, n_out),
+        None,
+        _addr(q, "q", b16, n_out),
+        _addr(k_pool, "k_pool", b16),
+        _addr(v_pool, "v_pool", b16),
+        _addr(block_table, "block_table", i32),
+        _addr(page_origin, "page_origin", i32, rows),
+        _addr(qpos, "qpos", i32, rows),
+        _addr(kv_last, "kv_last", i32, rows),
+    ]
+    if part is not None and not isinstance(part, int):
+        need = decode_part_bytes(rows, nh, splits, hd) if splits > 1 else 0
+        if not part.is_cuda or not part.is_contiguous() or part.numel() * part.element_size() < need:
+            raise PgqaError(EINVAL, f"part must be a contiguous device buffer of >= {need} bytes")
+        args[1] = part.data_ptr()
+    elif isinstance(part, int):
+        args[1] = part
+    cnt = _addr(counters, "counters", i32, counter_capacity())
+    pm = _addr(page_map, "page_map", i32)
+    if stream is None:
+        dev = out.device if hasattr(out, "device") else None
+        stream = torch.cuda.current_stream(dev).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = lib().pgqa_attn_decode(*args, rows, nh, nkv, hd, window, splits, cnt, pm, stream)
+    if rc != OK:
+        raise PgqaError(rc, last_error())

@@ -1,0 +1,56 @@
+"""Helpers for the GPU tests: upload a workload, run the C ABI through the
+binding, read results back.  Nothing here computes attention."""
+import numpy as np
+import torch
+
+import paged_gqa_decode_attn_amd as pg
+
+
+def dev_i16(a):
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def dev_i32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+
+
+class DeviceWorkload:
+    def __init__(self, w):
+        self.w = w
+        self.q = dev_i16(w.q)
+        self.k = dev_i16(w.k_pool)
+        self.v = dev_i16(w.v_pool)
+        self.bt = dev_i32(w.block_table)
+        self.off = dev_i32(w.page_origin)
+        self.qpos = dev_i32(w.qpos)
+        self.last = dev_i32(w.kv_last)
+        self.pmap = None if w.page_map is None else dev_i32(w.page_map)
+
+    def span(self):
+        w = self.w
+        ctx = int(w.kv_last.max()) + 1
+        return min(ctx, w.window) if w.window > 0 else ctx
+
+    def heuristic_splits(self, rows_per_seq=None):
+        w = self.w
+        return pg.choose_splits(self.span(), w.rows, w.nkv, w.rows if rows_per_seq is None else rows_per_seq)
+
+    def run(self, splits, counters=None, out=None, part=None, sync=True):
+        w = self.w
+        if out is None:
+            out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
+        if part is None and splits > 1:
+            part = torch.empty(pg.decode_part_bytes(w.rows, w.nh, splits, w.hd), dtype=torch.uint8,
+                               device="cuda")
+        pg.attn_decode(out, part, self.q, self.k, self.v, self.bt, self.off, self.qpos, self.last,
+                       w.rows, w.nh, w.nkv, w.hd, w.window, splits, counters, self.pmap)
+        if sync:
+            torch.cuda.synchronize()
+        return out
+
+    def host(self, out):
+        return out.cpu().numpy().view(np.uint16)
+
+
+def new_counters():
+    return torch.zeros(pg.counter_capacity(), dtype=torch.int32, device="cuda")

@@ -1,0 +1,105 @@
+"""Host-side checks of the C ABI that need no GPU: the library loads and
+exports every declared entry point; the split heuristic, buffer sizing and
+refusals behave as documented in include/pgqa.h.  Refused calls return before
+anything touches the HIP runtime, so they are safe without a device."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import paged_gqa_decode_attn_amd as pg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_functions():
+    text = open(os.path.join(ROOT, "include", "pgqa.h")).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(pgqa_\w+)\s*\(", text)))
+
+
+def test_library_exports_every_declared_symbol():
+    names = declared_functions()
+    assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
+            "pgqa_counter_capacity", "pgqa_last_error"} <= set(names)
+    h = ctypes.CDLL(pg.LIB_PATH)
+    for n in names:
+        assert getattr(h, n, None) is not None, n
+
+
+def test_counter_capacity():
+    assert pg.counter_capacity() == 4096
+
+
+def test_part_bytes_formula():
+    assert pg.decode_part_bytes(5, 16, 7, 256) == 5 * 16 * 7 * 258 * 4
+    assert pg.decode_part_bytes(1, 16, 256, 512) == 16 * 256 * 514 * 4
+    assert pg.decode_part_bytes(0, 16, 4, 64) == 0
+    assert pg.decode_part_bytes(1, 1, 0, 64) == 0
+
+
+def test_choose_splits_range_and_determinism():
+    for span in (1, 16, 64, 700, 1024, 4096, 32768, 131072, 1 << 20):
+        for rows in (1, 4, 8, 64, 512):
+            for nkv in (1, 2, 8):
+                for rps in (1, rows):
+                    s = pg.choose_splits(span, rows, nkv, rps)
+                    assert 1 <= s <= 256
+                    assert s == pg.choose_splits(span, rows, nkv, rps)
+                    # never more splits than pages
+                    assert s <= max(1, (span + 15) // 16)
+    # degenerate arguments fall back to one split
+    assert pg.choose_splits(0, 1, 1, 1) == 1
+    assert pg.choose_splits(100, 0, 1, 1) == 1
+    # a long single sequence gets many splits, a big batch few
+    assert pg.choose_splits(32768, 1, 2, 1) >= 64
+    assert pg.choose_splits(16384, 64, 8, 1) <= 4
+
+
+FAKE = 0x10000  # never dereferenced: every call below is refused first
+
+
+def call(**kw):
+    a = dict(out=FAKE, part=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, off=FAKE, qpos=FAKE,
+             last=FAKE, rows=1, nh=4, nkv=1, hd=64, window=0, splits=1, cnt=None, pmap=None)
+    a.update(kw)
+    return pg.lib().pgqa_attn_decode(a["out"], a["part"], a["q"], a["k"], a["v"], a["bt"],
+                                     a["off"], a["qpos"], a["last"], a["rows"], a["nh"],
+                                     a["nkv"], a["hd"], a["window"], a["splits"], a["cnt"],
+                                     a["pmap"], None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(out=None), pg.EINVAL),
+    (dict(q=None), pg.EINVAL),
+    (dict(k=None), pg.EINVAL),
+    (dict(v=None), pg.EINVAL),
+    (dict(bt=None), pg.EINVAL),
+    (dict(off=None), pg.EINVAL),
+    (dict(qpos=None), pg.EINVAL),
+    (dict(last=None), pg.EINVAL),
+    (dict(rows=0), pg.EINVAL),
+    (dict(nh=6, nkv=4), pg.EINVAL),
+    (dict(nkv=0), pg.EINVAL),
+    (dict(hd=96), pg.EINVAL),
+    (dict(hd=1024), pg.EINVAL),
+    (dict(window=-1), pg.EINVAL),
+    (dict(splits=0), pg.EINVAL),
+    (dict(splits=257), pg.EINVAL),
+    (dict(splits=4, part=None), pg.EINVAL),
+    (dict(q=FAKE + 8), pg.EINVAL),
+    (dict(splits=4, part=FAKE + 2), pg.EINVAL),
+    (dict(rows=4097, nkv=1, splits=2, cnt=FAKE), pg.ECAP),
+    (dict(rows=600, nh=64, nkv=8, splits=2, cnt=FAKE), pg.ECAP),
+])
+def test_refusals(kw, code):
+    assert call(**kw) == code
+    assert pg.last_error() != ""
+
+
+def test_missing_library_is_loud(tmp_path, monkeypatch):
+    monkeypatch.setattr(pg, "LIB_PATH", str(tmp_path / "nope.so"))
+    monkeypatch.setattr(pg, "_lib", None)
+    with pytest.raises(pg.PgqaError):
+        pg.lib()

@@ -1,0 +1,185 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle, and the
+bitwise gates of the span-02 GPU test page (fused merge == separate combine;
+identity pool == permuted pool behind a page map with a NaN null page).
+
+Tolerance: rel-RMS < 1e-2 against the oracle (the page's bound for decode).
+"""
+import functools
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():  # pragma: no cover - CPU container
+    pytest.skip("needs a GPU", allow_module_level=True)
+
+from tests.gpu_util import DeviceWorkload, new_counters  # noqa: E402
+
+TOL = 1e-2
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@functools.lru_cache(maxsize=None)
+def workload(name):
+    return workloads.make(name)
+
+
+@functools.lru_cache(maxsize=None)
+def reference(name):
+    return oracle.decode(workload(name))
+
+
+@functools.lru_cache(maxsize=2)
+def device(name):
+    return DeviceWorkload(workload(name))
+
+
+@pytest.fixture(scope="module")
+def counters():
+    return new_counters()
+
+
+def check_counters_zero(cnt):
+    assert int(cnt.abs().sum().item()) == 0, "merge counters not restored to zero"
+
+
+def gate(name, dw, splits, cnt, ref):
+    say(f"[gpu] {name} splits={splits}")
+    fused = dw.host(dw.run(splits, counters=cnt))
+    check_counters_zero(cnt)
+    sep = dw.host(dw.run(splits, counters=None))
+    assert np.array_equal(fused, sep), f"{name}: fused merge != separate combine at splits={splits}"
+    e = oracle.rel_rms(fused, ref)
+    say(f"[gpu] {name} splits={splits} rel_rms={e:.3e}")
+    assert e < TOL, (name, splits, e)
+    return fused
+
+
+@pytest.mark.parametrize("splits", [1, 4])
+def test_c1_tiny(counters, splits):
+    gate("C1", device("C1"), splits, counters, reference("C1"))
+
+
+@pytest.mark.parametrize("name", ["PA", "PB", "C2"])
+def test_page_configs_and_page_map(counters, name):
+    dw = device(name)
+    s = dw.heuristic_splits()
+    a = gate(name, dw, s, counters, reference(name))
+    wm = workloads.with_page_map(workload(name))
+    dm = DeviceWorkload(wm)
+    say(f"[gpu] {name}+pagemap splits={s}")
+    b = dm.host(dm.run(s, counters=counters))
+    check_counters_zero(counters)
+    assert np.array_equal(a, b), f"{name}: page-map pool differs"
+    for s2 in (1, 3, 16):
+        x = dw.host(dw.run(s2, counters=counters))
+        y = dm.host(dm.run(s2, counters=counters))
+        assert np.array_equal(x, y), (name, s2)
+        assert oracle.rel_rms(x, reference(name)) < TOL
+
+
+def test_c3_global_wide_head(counters):
+    dw = device("C3")
+    gate("C3", dw, dw.heuristic_splits(), counters, reference("C3"))
+
+
+@pytest.mark.parametrize("name", ["C4", "C4NAN"])
+def test_c4_batched(counters, name):
+    dw = device(name)
+    s = dw.heuristic_splits(rows_per_seq=1)
+    ref = reference("C4")  # NaN tails are outside every window: same answer
+    gate(name, dw, s, counters, ref)
+    if s != 3:
+        gate(name, dw, 3, counters, ref)
+
+
+@pytest.mark.parametrize("name", ["C5W0", "C5W4096"])
+def test_c5_long_multirow_split_sweep(counters, name):
+    dw = device(name)
+    ref = reference(name)
+    s_h = dw.heuristic_splits()
+    gate(name, dw, s_h, counters, ref)
+    say(f"[gpu] {name} sweeping splits 1..256")
+    for s in range(1, 257):
+        fused = dw.host(dw.run(s, counters=counters))
+        sep = dw.host(dw.run(s, counters=None))
+        assert np.array_equal(fused, sep), (name, s)
+        if s in (1, 2, 7, 64, 255, 256):
+            assert oracle.rel_rms(fused, ref) < TOL, (name, s)
+    check_counters_zero(counters)
+    if name == "C5W4096":
+        dm = DeviceWorkload(workloads.with_page_map(workload(name)))
+        for s in (1, s_h, 256):
+            a = dw.host(dw.run(s, counters=counters))
+            b = dm.host(dm.run(s, counters=counters))
+            assert np.array_equal(a, b), ("page map", s)
+
+
+@pytest.mark.parametrize("splits", [1, 2, 7, 64])
+def test_single_visible_key_is_exact(counters, splits):
+    """window = 1: the output is the V row of the query position, bit for bit."""
+    w = workload("PA").replace(window=1)
+    dw = DeviceWorkload(w)
+    out = dw.host(dw.run(splits, counters=counters))
+    g = w.nh // w.nkv
+    for t in range(w.rows):
+        p = int(w.qpos[t])
+        for h in range(w.nh):
+            assert np.array_equal(out[t, h], w.v_pool[int(w.block_table[p // 16]), h // g, p % 16])
+
+
+def edge_workloads():
+    rng_seq = workloads.single_sequence
+    cases = []
+    # rows of several sequences: runs of equal origin cut by origin changes and
+    # by the tile size, distinct positions inside a run, ragged row count
+    b = workloads.batched("mixed", nseq=4, lmin=40, lmax=300, nh=8, nkv=2, hd=128, pad=16)
+    seq = np.array([0, 0, 1, 2, 2, 2, 2, 2, 3])
+    back = np.array([1, 0, 0, 4, 3, 2, 1, 0, 0])
+    qp = (b.qpos[seq] - back).astype(np.int32)
+    cases.append(b.replace(name="mixed", rows=len(seq), q=np.concatenate([b.q, b.q, b.q])[:len(seq)],
+                           page_origin=b.page_origin[seq].copy(), qpos=qp, kv_last=qp.copy()))
+    # wide group (32 heads per kv head -> two head blocks), nkv=1
+    cases.append(rng_seq("g32", ctx=333, rows=2, nh=32, nkv=1, hd=64, window=0))
+    # plain MHA (group 1): 16 rows share each page
+    cases.append(rng_seq("mha", ctx=257, rows=19, nh=4, nkv=4, hd=128, window=100))
+    # window larger than the context, partial first page, hd 512, 3 rows (group 8 -> 2 per tile)
+    cases.append(rng_seq("wbig", ctx=181, rows=3, nh=16, nkv=2, hd=512, window=5000))
+    # rows whose last visible key is below the query position (second position array)
+    w2 = rng_seq("kvlast", ctx=500, rows=4, nh=8, nkv=2, hd=256, window=0)
+    cases.append(w2.replace(name="kvlast", kv_last=np.array([100, 499, 300, 498], np.int32)))
+    # an empty visible set (last key below the window start) -> zeros
+    w3 = rng_seq("empty", ctx=200, rows=2, nh=4, nkv=1, hd=64, window=8)
+    cases.append(w3.replace(name="empty", kv_last=np.array([150, 199], np.int32)))
+    return cases
+
+
+@pytest.mark.parametrize("w", edge_workloads(), ids=lambda w: w.name)
+def test_edge_cases(counters, w):
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    ctx = int(w.kv_last.max()) + 1
+    pages = (ctx + 15) // 16
+    for s in sorted({1, 2, 5, min(256, pages + 3)}):
+        gate(w.name, dw, s, counters, ref)
+    if w.name == "empty":
+        out = dw.host(dw.run(4, counters=counters))
+        assert not out[0].any()
+
+
+def test_counter_capacity_refusal():
+    import paged_gqa_decode_attn_amd as pg
+    w = workloads.single_sequence("cap", ctx=4200, rows=4097, nh=1, nkv=1, hd=64, window=0)
+    dw = DeviceWorkload(w)
+    with pytest.raises(pg.PgqaError) as ei:
+        dw.run(2, counters=new_counters())
+    assert ei.value.code == pg.ECAP
