@@ -350,6 +350,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   __syncthreads();
   if (wave == 1) put_state(0);
   __syncthreads();
+  if (wave == 0) take_state(0);
 
   const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
   if (wave == 0) {
