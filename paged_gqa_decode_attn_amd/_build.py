@@ -14,6 +14,9 @@ FLAGS = [
     "-Wall", "-Wno-unused-command-line-argument",
     # packed-FP32 VALU ops stay off (device side; the host pass ignores it)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA accumulators in VGPRs: no AGPR<->VGPR copies around the VALU
+    # rescaling of the output accumulators
+    "-mllvm", "-amdgpu-mfma-vgpr-form=1",
 ]
 
 

@@ -39,6 +39,7 @@
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
+#include <type_traits>
 
 #include "pgqa.h"
 
@@ -89,27 +90,108 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Merge of S split partials for one output element, in split order.  Used by
-// both the fused last-workgroup merge and the combine kernel: the only merge
-// arithmetic in the library, with explicit fused multiply-adds so both callers
-// compile to the same operations.
-__device__ __forceinline__ float merge_splits(const float *__restrict__ o, const float *__restrict__ ml,
-                                              int splits, int hd, int d) {
-  float mx = -INFINITY;
-  for (int s = 0; s < splits; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.f) mx = fmaxf(mx, ml[2 * s]);
+// Agent-coherent 32-bit accesses for data exchanged between workgroups inside
+// one launch (the fused merge).  They go past this XCD's L2, so no L2
+// write-back fence is needed; ordering comes from waiting for the stores to
+// complete before the counter ticket, and from the ticket's result gating the
+// loads.
+__device__ __forceinline__ void store_coherent(float *p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+struct LoadPlain {
+  __device__ __forceinline__ float operator()(const float *p) const { return *p; }
+};
+struct LoadCoherent {
+  __device__ __forceinline__ float operator()(const float *p) const {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
-  float num = 0.f, den = 0.f;
-  for (int s = 0; s < splits; ++s) {
-    const float l = ml[2 * s + 1];
-    if (l > 0.f) {
-      const float w = fast_exp2(ml[2 * s] - mx);
-      den = __builtin_fmaf(w, l, den);
-      num = __builtin_fmaf(w, o[static_cast<int64_t>(s) * hd + d], num);
+};
+__device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0); }
+
+// ---- cross-split merge -------------------------------------------------
+// The merge of S split partials (o_s[hd], m_s, l_s) of one (row, query head):
+//   M   = max m_s over non-empty splits (l_s > 0),  w_s = exp2(m_s - M) (else 0)
+//   num = sum_g ( sum_{s = g mod 8, s ascending} w_s o_s[d] ),  g = 0..7 in order
+//   den = the same grouping over w_s l_s,  out = num / den  (0 if den == 0).
+// The eight strided groups let the loads of a merge run in parallel; the order
+// is fixed, and both the fused last-workgroup merge and the combine kernel run
+// this exact code (they differ only in how the partials are loaded), so the
+// two paths give the same bits.
+constexpr int kMergeGroups = 8;
+constexpr int kMergeChunk = 128;  // hd elements merged per pass
+
+// LDS scratch of a merge: split weights, split sums, reductions, group sums.
+struct MergeScratch {
+  float w[kMaxSplits];
+  float l[kMaxSplits];
+  float red[16];
+  float acc[kMergeGroups][kMergeChunk];
+};
+
+// Fills ms.w / ms.l for one (row, head) and returns the denominator.  Every
+// thread of the (256-thread) workgroup calls it.
+template <class Load>
+__device__ float merge_weights(Load ld, const float *ml, int splits, MergeScratch &ms) {
+  const int tid = threadIdx.x;
+  float m = -INFINITY, l = 0.f;
+  if (tid < splits) {
+    l = ld(ml + 2 * tid + 1);
+    if (l > 0.f) m = ld(ml + 2 * tid);
+  }
+  float mx = m;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) ms.red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(ms.red[0], ms.red[1]), fmaxf(ms.red[2], ms.red[3]));
+  ms.w[tid] = (tid < splits && l > 0.f) ? fast_exp2(m - mx) : 0.f;
+  ms.l[tid] = l;
+  __syncthreads();
+  if (tid < kMergeGroups) {
+    float dg = 0.f;
+    for (int s = tid; s < splits; s += kMergeGroups) {
+      const float ws = ms.w[s];
+      dg = ws != 0.f ? __builtin_fmaf(ws, ms.l[s], dg) : dg;
+    }
+    ms.red[8 + tid] = dg;
+  }
+  __syncthreads();
+  float den = 0.f;
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) den += ms.red[8 + g];
+  return den;
+}
+
+// Merges hd elements d0 .. d0 + 32*NB - 1 of one (row, head) and writes them
+// as bf16 to out_row[d].  Thread (g, e) = (tid / 32, tid % 32) accumulates
+// group g for elements d0 + 32*b + e.
+template <int NB, class Load>
+__device__ void merge_chunk(Load ld, const float *o, int splits, int hd, int d0, float den, MergeScratch &ms,
+                            uint16_t *out_row) {
+  const int tid = threadIdx.x;
+  const int g = tid >> 5, e = tid & 31;
+  float num[NB];
+#pragma unroll
+  for (int b = 0; b < NB; ++b) num[b] = 0.f;
+  for (int s = g; s < splits; s += kMergeGroups) {
+    const float ws = ms.w[s];
+    const float *os = o + static_cast<int64_t>(s) * hd + d0 + e;
+#pragma unroll
+    for (int b = 0; b < NB; ++b) {
+      const float v = ld(os + 32 * b);
+      num[b] = ws != 0.f ? __builtin_fmaf(ws, v, num[b]) : num[b];
     }
   }
-  return den > 0.f ? num / den : 0.f;
+#pragma unroll
+  for (int b = 0; b < NB; ++b) ms.acc[g][32 * b + e] = num[b];
+  __syncthreads();
+  if (tid < 32 * NB) {
+    float n = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < kMergeGroups; ++gg) n += ms.acc[gg][tid];
+    out_row[d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
+  }
+  __syncthreads();
 }
 
 // Column c (0..15) of a tile -> (row offset, head within the kv group), or
@@ -132,6 +214,11 @@ __device__ __forceinline__ Column tile_column(int c, int group, int nrows, int h
   return col;
 }
 
+// The running max of a column only moves when a page's max exceeds it by more
+// than this (log2 units), so the output accumulators are rescaled rarely;
+// softmax weights then stay below 2^kRescaleSlack.
+constexpr float kRescaleSlack = 8.f;
+
 template <int HD>
 __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;   // QK^T MFMA steps (32 hd elements each)
@@ -143,9 +230,10 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   __shared__ float xfer[kWaves][16];
   __shared__ int s_is_last;
   static_assert(2 * (16 * HD + 32) * 4 <= kWaves * kPage * VSTR * 2, "merge slots must fit the V staging area");
+  static_assert(sizeof(MergeScratch) <= sizeof(vtile), "merge scratch must fit the V staging area");
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int ln = lane & 15;  // MFMA row/column index of this lane
   const int lc = lane >> 4;  // MFMA k-group of this lane
 
@@ -158,23 +246,42 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   const int t0 = b / a.nkv;
 
   // ---- tile: rows t0 .. t0+nrows-1 share the origin; t0 must lead it ----
-  const int origin = a.page_origin[t0];
-  if (t0 % a.rmax != 0 && a.page_origin[t0 - 1] == origin) return;
-  int nrows = 1;
-  while (nrows < a.rmax && t0 + nrows < a.rows && (t0 + nrows) % a.rmax != 0 &&
-         a.page_origin[t0 + nrows] == origin)
-    ++nrows;
-
-  int lo_min = INT_MAX, hi_max = -1;
-  for (int r = 0; r < nrows; ++r) {
-    const int qp = a.qpos[t0 + r];
-    const int hi = a.kv_last[t0 + r];
-    const int lo = a.window > 0 ? max(0, qp + 1 - a.window) : 0;
-    if (hi >= lo) {
-      lo_min = min(lo_min, lo);
-      hi_max = max(hi_max, hi);
+  // Lane r (< rmax) reads row t0 + r; Q for every possible column is requested
+  // in the same round, before the tile is known.
+  const bool lrow = lane < a.rmax && t0 + lane < a.rows;
+  const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
+  const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
+  const int hi_l = lrow ? a.kv_last[t0 + lane] : -1;
+  const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
+  const Column col0 = tile_column(ln, a.group, a.rmax, hb);  // before the row count is known
+  bf16x8 qop[KJ];
+  {
+    const bool q_in = col0.on && t0 + col0.row < a.rows;
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (q_in ? col0.row : 0)) * a.nh + kh * a.group + col0.head) * HD;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j) {
+      if (q_in) {
+        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[j] = __builtin_bit_cast(bf16x8, z);
+      }
     }
   }
+  const int origin = __builtin_amdgcn_readfirstlane(org_l);
+  if (t0 % a.rmax != 0 && prev_origin == origin) return;
+  const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != origin || (t0 + lane) % a.rmax == 0));
+  const int nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
+  const int lo_l = a.window > 0 ? max(0, qp_l + 1 - a.window) : 0;
+  const bool live = lane < nrows && hi_l >= lo_l;
+  int lo_min = live ? lo_l : INT_MAX, hi_max = live ? hi_l : -1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo_min = min(lo_min, __shfl_xor(lo_min, off));
+    hi_max = max(hi_max, __shfl_xor(hi_max, off));
+  }
+  lo_min = __builtin_amdgcn_readfirstlane(lo_min);
+  hi_max = __builtin_amdgcn_readfirstlane(hi_max);
   int pbeg = 0, pend = 0;
   if (hi_max >= 0) {
     const int p0 = lo_min / kPage;
@@ -185,41 +292,67 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
 
   // ---- this lane's score column ----
   const Column col = tile_column(ln, a.group, nrows, hb);
-  const int col_t = t0 + (col.on ? col.row : 0);
-  const int col_h = kh * a.group + col.head;
-  int col_lo = 0, col_hi = -1;
-  if (col.on) {
-    const int qp = a.qpos[col_t];
-    col_hi = a.kv_last[col_t];
-    col_lo = a.window > 0 ? max(0, qp + 1 - a.window) : 0;
-  }
-
-  // Q^T as the B operand: step j, lane (ln, lc) holds hd elements (4j+lc)*8..+8
-  // of column ln -- the same hd chunk the K operand lanes load for step j.
-  bf16x8 qop[KJ];
-  {
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(col_t) * a.nh + col_h) * HD;
+  const int col_lo = __shfl(lo_l, col.row);
+  const int col_hi = col.on ? __shfl(hi_l, col.row) : -1;
+  if (!col.on) {
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      if (col.on) {
-        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
-      } else {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qop[j] = __builtin_bit_cast(bf16x8, z);
-      }
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qop[j] = __builtin_bit_cast(bf16x8, z);
     }
   }
 
-  float m_run = -INFINITY;  // running max (log2 units) of column ln
+  float m_run = -INFINITY;  // reference max (log2 units) of column ln
   f32x4 oacc[DJ];           // rows 4*lc+i of the column block, hd column 16*jj+ln
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int jj = 0; jj < DJ; ++jj) oacc[jj] = f32x4{0.f, 0.f, 0.f, 0.f};
   const s16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
   const int64_t kv_head_off = static_cast<int64_t>(kh) * kPage * HD;
+  const int64_t page_elems = static_cast<int64_t>(a.nkv) * kPage * HD;
   uint16_t *vt = vtile[wave];
+  // V operand of step jj via the LDS transpose read: lane (4m+q) of k-group lc
+  // points at token row 4*lc+m, hd column 16*jj + 4q, and receives
+  // V[4*lc .. 4*lc+3][16*jj + ln] (the 16 lanes' 4-element rows are
+  // redistributed column-wise).
+  const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * VSTR + 4 * (ln & 3);
 
-  for (int p = pbeg + wave; p < pend; p += kWaves) {
+  // This wave's pages: pbeg + wave + kWaves * k, k = 0 .. nk-1.  They are
+  // walked in windows of 128; the physical pages of a window are fetched (lane
+  // l of pv0 / pv1: page w0 + l / w0 + 64 + l) and waited for before the
+  // window's pipelined loop, so page loads never wait on the table.
+  const int first = pbeg + wave;
+  const int nk = first < pend ? (pend - first + kWaves - 1) / kWaves : 0;
+  int pv0 = 0, pv1 = 0;
+  auto fetch_window = [&](int w0) {
+    int ph[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = w0 + 64 * h + lane;
+      ph[h] = 0;
+      if (k < nk) {
+        ph[h] = a.block_table[origin + first + kWaves * k];
+        if (a.page_map) ph[h] = a.page_map[ph[h]];
+      }
+    }
+    pv0 = ph[0];
+    pv1 = ph[1];
+    wait_all_memory();
+  };
+  auto load_page = [&](int kw, bf16x8(&kop)[KJ], u32x4(&vreg)[VLD]) {
+    const int phys = kw < 64 ? __builtin_amdgcn_readlane(pv0, kw) : __builtin_amdgcn_readlane(pv1, kw - 64);
+    const int64_t page_off = static_cast<int64_t>(phys) * page_elems + kv_head_off;
+    const uint16_t *kp = a.k_pool + page_off;
+    const uint16_t *vp = a.v_pool + page_off;
+#pragma unroll
+    for (int j = 0; j < KJ; ++j)
+      kop[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(kp + ln * HD + (4 * j + lc) * 8));
+#pragma unroll
+    for (int j = 0; j < VLD; ++j)
+      vreg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + (j * 64 + lane) * 8));
+  };
+  auto compute_page = [&](int k, const bf16x8(&kop)[KJ], const u32x4(&vreg)[VLD]) {
+    const int p = first + kWaves * k;
     // Visibility of the 4 tokens this lane scores, and of each token for any column.
     const int pos0 = p * kPage + 4 * lc;
     bool vis[4];
@@ -232,22 +365,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
       for (int g = 0; g < 4; ++g)
         if ((bal >> (16 * g)) & 0xffffull) tokmask |= 1u << (4 * g + i);
     }
-    if (tokmask == 0) continue;
-
-    int phys = a.block_table[origin + p];
-    if (a.page_map) phys = a.page_map[phys];
-    const int64_t page_off = static_cast<int64_t>(phys) * a.nkv * kPage * HD + kv_head_off;
-    const uint16_t *kp = a.k_pool + page_off;
-    const uint16_t *vp = a.v_pool + page_off;
-
-    bf16x8 kop[KJ];
-#pragma unroll
-    for (int j = 0; j < KJ; ++j)
-      kop[j] = *reinterpret_cast<const bf16x8 *>(kp + ln * HD + (4 * j + lc) * 8);
-    u32x4 vreg[VLD];
-#pragma unroll
-    for (int j = 0; j < VLD; ++j)
-      vreg[j] = *reinterpret_cast<const u32x4 *>(vp + (j * 64 + lane) * 8);
+    if (tokmask == 0) return;
 
     // S^T: lane holds scores of tokens 4*lc+i for column ln.
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
@@ -263,25 +381,27 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m_run, mx);
-    const bool none = m_new == -INFINITY;
-    const float alpha = none ? 1.f : fast_exp2(m_run - m_new);
+    // Move the reference max only when this page exceeds it by the slack.
+    const bool grow = mx > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? mx : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      // factors move from the column layout (lane ln) to the output layout
+      // (lane holds rows 4*lc .. 4*lc+3)
+      if (lc == 0) xfer[wave][ln] = alpha;
+      wave_lds_sync();
+      const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+#pragma unroll
+      for (int jj = 0; jj < DJ; ++jj) oacc[jj] *= al;
+      lacc *= al;
+    }
     s16x4 pa;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pr = none ? 0.f : fast_exp2(s2[i] - m_new);
+      const float pr = vis[i] ? fast_exp2(s2[i] - m_run) : 0.f;
       pa[i] = static_cast<short>(f32_to_bf16_rne(pr));
     }
-    m_run = m_new;
-
-    // Rescale factors move from the column layout (lane ln) to the output layout
-    // (lane holds rows 4*lc .. 4*lc+3).
-    if (lc == 0) xfer[wave][ln] = alpha;
-    wave_lds_sync();
-    const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
-#pragma unroll
-    for (int jj = 0; jj < DJ; ++jj) oacc[jj] *= al;
-    lacc *= al;
 
     // Stage V; tokens no column can see are zeroed (they may hold NaN).
 #pragma unroll
@@ -295,16 +415,43 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
     wave_lds_sync();
 #pragma unroll
     for (int jj = 0; jj < DJ; ++jj) {
-      s16x4 vb;
-#pragma unroll
-      for (int r = 0; r < 4; ++r) vb[r] = static_cast<short>(vt[(4 * lc + r) * VSTR + 16 * jj + ln]);
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(vtr + 16 * jj));
       oacc[jj] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, oacc[jj], 0, 0, 0);
     }
     lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
     wave_lds_sync();
+  };
+
+  // Two register sets (hd <= 256): the next page's K and V are in flight while
+  // the current page is computed; past the window's end its last page is
+  // loaded again (already cached) so every step issues the same loads.  At
+  // hd 512 the registers hold one page only.
+  for (int w0 = 0; w0 < nk; w0 += 128) {
+    const int wn = min(128, nk - w0);
+    fetch_window(w0);
+    bf16x8 kA[KJ];
+    u32x4 vA[VLD];
+    load_page(0, kA, vA);
+    if constexpr (HD <= 256) {
+      bf16x8 kB[KJ];
+      u32x4 vB[VLD];
+      for (int k = 0; k < wn; k += 2) {
+        load_page(min(k + 1, wn - 1), kB, vB);
+        compute_page(w0 + k, kA, vA);
+        load_page(min(k + 2, wn - 1), kA, vA);
+        if (k + 1 < wn) compute_page(w0 + k + 1, kB, vB);
+      }
+    } else {
+      for (int k = 0; k < wn; ++k) {
+        if (k > 0) load_page(k, kA, vA);
+        compute_page(w0 + k, kA, vA);
+      }
+    }
+    wait_all_memory();
   }
 
-  // ---- running max into the output layout ----
+  // ---- reference max into the output layout ----
   if (lc == 0) xfer[wave][ln] = m_run;
   wave_lds_sync();
   f32x4 mo = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
@@ -353,6 +500,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   if (wave == 0) take_state(0);
 
   const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
+  const bool fused = a.splits > 1 && a.counters != nullptr;
   if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -370,46 +518,58 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
       } else {
         const int64_t ps = th * a.splits + split;
         float *po = a.part_o + ps * HD;
+        if (fused) {
 #pragma unroll
-        for (int jj = 0; jj < DJ; ++jj) po[16 * jj + ln] = oacc[jj][i];
-        if (ln == 0) {
-          a.part_ml[2 * ps] = mo[i];
-          a.part_ml[2 * ps + 1] = lacc[i];
+          for (int jj = 0; jj < DJ; ++jj) store_coherent(po + 16 * jj + ln, oacc[jj][i]);
+          if (ln == 0) {
+            store_coherent(a.part_ml + 2 * ps, mo[i]);
+            store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
+          }
+        } else {
+#pragma unroll
+          for (int jj = 0; jj < DJ; ++jj) po[16 * jj + ln] = oacc[jj][i];
+          if (ln == 0) {
+            a.part_ml[2 * ps] = mo[i];
+            a.part_ml[2 * ps + 1] = lacc[i];
+          }
         }
       }
     }
   }
-  if (a.splits == 1 || a.counters == nullptr) return;
+  if (!fused) return;
 
   // ---- fused merge: the last workgroup of this unit merges every split ----
-  __threadfence();
+  wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
   const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
   if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
+    const int prev = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     s_is_last = prev == a.splits - 1;
   }
   __syncthreads();
   if (!s_is_last) return;
-  __threadfence();
-  for (int idx = threadIdx.x; idx < ncols * HD; idx += kThreads) {
-    const int c = idx / HD;
-    const int d = idx - c * HD;
+  MergeScratch &ms = *reinterpret_cast<MergeScratch *>(&vtile[0][0]);
+  for (int c = 0; c < ncols; ++c) {
     const Column rc = tile_column(c, a.group, nrows, hb);
     const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-    const float v = merge_splits(a.part_o + th * a.splits * HD, a.part_ml + th * a.splits * 2, a.splits, HD, d);
-    a.out[th * HD + d] = f32_to_bf16_rne(v);
+    const float den = merge_weights(LoadCoherent{}, a.part_ml + th * a.splits * 2, a.splits, ms);
+#pragma unroll 1
+    for (int d0 = 0; d0 < HD; d0 += kMergeChunk)
+      merge_chunk<(HD < kMergeChunk ? HD : kMergeChunk) / 32>(LoadCoherent{}, a.part_o + th * a.splits * HD, a.splits, HD, d0,
+                                                               den, ms, a.out + th * HD);
   }
   if (threadIdx.x == 0) __hip_atomic_store(&a.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// Separate merge: one workgroup per (row, query head).
-__global__ __launch_bounds__(256) void pgqa_combine_kernel(DecodeArgs a, int hd) {
-  const int64_t th = blockIdx.x;
-  const float *po = a.part_o + th * a.splits * hd;
-  const float *pml = a.part_ml + th * a.splits * 2;
-  for (int d = threadIdx.x; d < hd; d += blockDim.x)
-    a.out[th * hd + d] = f32_to_bf16_rne(merge_splits(po, pml, a.splits, hd, d));
+// Separate merge: one workgroup per (row, query head, chunk of hd).
+template <int NB>
+__global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, int hd) {
+  __shared__ MergeScratch ms;
+  const int chunks = hd / (32 * NB);
+  const int64_t th = blockIdx.x / chunks;
+  const int d0 = (blockIdx.x - th * chunks) * 32 * NB;
+  const float den = merge_weights(LoadPlain{}, a.part_ml + th * a.splits * 2, a.splits, ms);
+  merge_chunk<NB>(LoadPlain{}, a.part_o + th * a.splits * hd, a.splits, hd, d0, den, ms, a.out + th * hd);
 }
 
 thread_local char g_error[512] = "";
@@ -488,7 +648,7 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   const int64_t units = rows * nkv * hblocks;
   if (counters && splits > 1 && units > kCounterCap)
     return fail(PGQA_ECAP, "%lld merge units exceed the %d counters", (long long)units, kCounterCap);
-  if (rows * nh > INT_MAX) return fail(PGQA_EINVAL, "rows * nh too large");
+  if (rows * nh * (hd > 128 ? hd / 128 : 1) > INT_MAX) return fail(PGQA_EINVAL, "rows * nh too large");
   const int64_t blocks = units * splits;
   if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
 
@@ -524,8 +684,12 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {
-    hipLaunchKernelGGL(pgqa_combine_kernel, dim3(static_cast<unsigned>(rows * nh)), dim3(256), 0, st, a,
-                       static_cast<int>(hd));
+    if (hd == 64)
+      hipLaunchKernelGGL(pgqa_combine_kernel<2>, dim3(static_cast<unsigned>(rows * nh)), dim3(kThreads), 0, st, a,
+                         static_cast<int>(hd));
+    else
+      hipLaunchKernelGGL(pgqa_combine_kernel<4>, dim3(static_cast<unsigned>(rows * nh * (hd / 128))), dim3(kThreads), 0,
+                         st, a, static_cast<int>(hd));
     err = hipGetLastError();
     if (err != hipSuccess) return fail(PGQA_ELAUNCH, "combine kernel launch: %s", hipGetErrorString(err));
   }
