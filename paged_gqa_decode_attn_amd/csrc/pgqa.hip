@@ -71,6 +71,7 @@ struct DecodeArgs {
   int32_t *counters;
   const int32_t *page_map;
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
+  int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
 };
 
 // Orders this wave's LDS accesses around the point (a wave executes its LDS
@@ -78,6 +79,21 @@ struct DecodeArgs {
 __device__ __forceinline__ void wave_lds_sync() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// 16-byte direct load global -> LDS: every lane's 16 bytes land at
+// lds_base + 16 * lane (lds_base must be the same for the whole wave).
+__device__ __forceinline__ void load_to_lds16(const void *src, void *lds_base) {
+  __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
+}
+
+// Workgroup barrier for LDS exchanges only: waits for this wave's LDS traffic,
+// not for its vector-memory loads (which stay in flight across it).
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_s_waitcnt(0xc07f);  // lgkmcnt(0); vmcnt and expcnt unconstrained
+  __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
@@ -89,6 +105,17 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
 }
 
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+typedef __attribute__((ext_vector_type(2))) float f32x2;
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+// Four softmax weights -> bf16 (round to nearest even, v_cvt_pk_bf16_f32).
+__device__ __forceinline__ s16x4 pack_weights(float p0, float p1, float p2, float p3) {
+  const bf16x2 lo = __builtin_convertvector(f32x2{p0, p1}, bf16x2);
+  const bf16x2 hi = __builtin_convertvector(f32x2{p2, p3}, bf16x2);
+  const unsigned u0 = __builtin_bit_cast(unsigned, lo), u1 = __builtin_bit_cast(unsigned, hi);
+  return s16x4{static_cast<short>(u0 & 0xffff), static_cast<short>(u0 >> 16), static_cast<short>(u1 & 0xffff),
+               static_cast<short>(u1 >> 16)};
+}
 
 // Agent-coherent 32-bit accesses for data exchanged between workgroups inside
 // one launch (the fused merge).  They go past this XCD's L2, so no L2
@@ -128,6 +155,15 @@ struct MergeScratch {
   float acc[kMergeGroups][kMergeChunk];
 };
 
+// LDS scratch of the fused merge: weights and sums of up to kThreads
+// (column, split) pairs, per-column max and denominator.
+struct FusedScratch {
+  float w[kThreads];
+  float l[kThreads];
+  float mx[kThreads];
+  float den[kThreads];
+};
+
 // Fills ms.w / ms.l for one (row, head) and returns the denominator.  Every
 // thread of the (256-thread) workgroup calls it.
 template <class Load>
@@ -135,8 +171,9 @@ __device__ float merge_weights(Load ld, const float *ml, int splits, MergeScratc
   const int tid = threadIdx.x;
   float m = -INFINITY, l = 0.f;
   if (tid < splits) {
+    const float mm = ld(ml + 2 * tid);
     l = ld(ml + 2 * tid + 1);
-    if (l > 0.f) m = ld(ml + 2 * tid);
+    if (l > 0.f) m = mm;
   }
   float mx = m;
 #pragma unroll
@@ -173,13 +210,24 @@ __device__ void merge_chunk(Load ld, const float *o, int splits, int hd, int d0,
   float num[NB];
 #pragma unroll
   for (int b = 0; b < NB; ++b) num[b] = 0.f;
-  for (int s = g; s < splits; s += kMergeGroups) {
-    const float ws = ms.w[s];
-    const float *os = o + static_cast<int64_t>(s) * hd + d0 + e;
+  // 4 splits of this group per step, all loads issued before any is used
+  for (int s = g; s < splits; s += 4 * kMergeGroups) {
+    float v[4][NB];
 #pragma unroll
-    for (int b = 0; b < NB; ++b) {
-      const float v = ld(os + 32 * b);
-      num[b] = ws != 0.f ? __builtin_fmaf(ws, v, num[b]) : num[b];
+    for (int u = 0; u < 4; ++u) {
+      const int su = min(s + u * kMergeGroups, splits - 1);
+      const float *os = o + static_cast<int64_t>(su) * hd + d0 + e;
+#pragma unroll
+      for (int b = 0; b < NB; ++b) v[u][b] = ld(os + 32 * b);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int su = s + u * kMergeGroups;
+      if (su < splits) {
+        const float ws = ms.w[su];
+#pragma unroll
+        for (int b = 0; b < NB; ++b) num[b] = ws != 0.f ? __builtin_fmaf(ws, v[u][b], num[b]) : num[b];
+      }
     }
   }
 #pragma unroll
@@ -194,24 +242,182 @@ __device__ void merge_chunk(Load ld, const float *o, int splits, int hd, int d0,
   __syncthreads();
 }
 
-// Column c (0..15) of a tile -> (row offset, head within the kv group), or
-// off if the tile has no such column.
+// Column c (0 .. cap-1) of a tile -> (row offset, head within the kv group),
+// or off if the tile has no such column.  A group of at most `cap` heads keeps
+// whole rows in a tile; a wider group is cut into head blocks of `cap`.
 struct Column {
   int row, head;
   bool on;
 };
-__device__ __forceinline__ Column tile_column(int c, int group, int nrows, int hb) {
+__device__ __forceinline__ Column tile_column(int c, int group, int nrows, int hb, int cap) {
   Column col;
-  if (group <= 16) {
+  if (group <= cap) {
     col.row = c / group;
     col.head = c - col.row * group;
     col.on = col.row < nrows;
   } else {
     col.row = 0;
-    col.head = hb * 16 + c;
+    col.head = hb * cap + c;
     col.on = col.head < group;
   }
   return col;
+}
+
+// Rows t0 .. t0+nrows-1 (nrows <= rmax) that share row t0's page origin and
+// stay inside one rmax-aligned block.  Lane r < rmax keeps row t0 + r's
+// visible range [lo_l, hi_l]; lo_min / hi_max span the tile's rows.  A
+// workgroup whose t0 does not start a tile has nothing to do (lead false).
+struct Tile {
+  int origin, nrows, lo_l, hi_l, lo_min, hi_max;
+  int fp0, fp1;  // pages [fp0, fp1) are visible in full to every row of the tile
+  bool lead;
+};
+__device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane) {
+  Tile t;
+  const bool lrow = lane < a.rmax && t0 + lane < a.rows;
+  const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
+  const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
+  t.hi_l = lrow ? a.kv_last[t0 + lane] : -1;
+  const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
+  t.origin = __builtin_amdgcn_readfirstlane(org_l);
+  t.lead = t0 % a.rmax == 0 || prev_origin != t.origin;
+  const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin || (t0 + lane) % a.rmax == 0));
+  t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
+  t.lo_l = a.window > 0 ? max(0, qp_l + 1 - a.window) : 0;
+  const bool live = lane < t.nrows && t.hi_l >= t.lo_l;
+  int lo = live ? t.lo_l : INT_MAX, hi = live ? t.hi_l : -1;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo = min(lo, __shfl_xor(lo, off));
+    hi = max(hi, __shfl_xor(hi, off));
+  }
+  t.lo_min = __builtin_amdgcn_readfirstlane(lo);
+  t.hi_max = __builtin_amdgcn_readfirstlane(hi);
+  int lo_all = lane < t.nrows ? t.lo_l : INT_MIN, hi_all = lane < t.nrows ? t.hi_l : INT_MAX;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    lo_all = max(lo_all, __shfl_xor(lo_all, off));
+    hi_all = min(hi_all, __shfl_xor(hi_all, off));
+  }
+  lo_all = __builtin_amdgcn_readfirstlane(lo_all);
+  hi_all = __builtin_amdgcn_readfirstlane(hi_all);
+  t.fp0 = (lo_all + kPage - 1) / kPage;
+  t.fp1 = hi_all >= lo_all ? (hi_all + 1) / kPage : t.fp0;
+  return t;
+}
+
+// Split `split` of S covers pages [pbeg, pend) of the tile's visible page
+// range [lo_min / 16, hi_max / 16], cut into S contiguous near-equal chunks
+// from logical positions only (some may be empty).
+__device__ __forceinline__ void split_range(const Tile &t, int split, int splits, int &pbeg, int &pend) {
+  pbeg = pend = 0;
+  if (t.hi_max >= 0) {
+    const int p0 = t.lo_min / kPage;
+    const int64_t npg = t.hi_max / kPage - p0 + 1;
+    pbeg = p0 + static_cast<int>(npg * split / splits);
+    pend = p0 + static_cast<int>(npg * (split + 1) / splits);
+  }
+}
+
+// ---- fused merge: the last workgroup of a merge unit merges every split ----
+// Called by all threads once this workgroup's partial stores are issued.  The
+// unit's counter is a ticket: the workgroup that draws splits-1 merges and
+// resets the counter to zero.  Columns are taken CG at a time (CG * S <= 256):
+// one round of loads fetches every (m, l) of the group, a second every partial
+// element; each thread keeps the eight group sums of its elements, which is
+// the combine kernel's arithmetic element for element.
+template <int HD>
+__device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
+                            FusedScratch *fsp, int *s_is_last) {
+  wait_all_memory();  // this workgroup's partial stores have completed
+  __syncthreads();
+  const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
+  if (threadIdx.x == 0) {
+    const int prev = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    *s_is_last = prev == a.splits - 1;
+  }
+  __syncthreads();
+  if (!*s_is_last) return;
+  FusedScratch &fs = *fsp;
+  const LoadCoherent ld;
+  const int S = a.splits;
+  const int tid = threadIdx.x;
+  const int cg_max = max(1, min(ncols, kThreads / S));
+  for (int c0 = 0; c0 < ncols; c0 += cg_max) {
+    const int cg = min(cg_max, ncols - c0);
+    // (m, l) of every (column, split) of the group
+    for (int idx = tid; idx < cg * S; idx += kThreads) {
+      const int c = idx / S, sp = idx - c * S;
+      const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
+      const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+      const float m = ld(a.part_ml + (th * S + sp) * 2);
+      const float l = ld(a.part_ml + (th * S + sp) * 2 + 1);
+      fs.l[idx] = l;
+      fs.w[idx] = l > 0.f ? m : -INFINITY;
+    }
+    __syncthreads();
+    if (tid < cg) {
+      float mx = -INFINITY;
+      for (int sp = 0; sp < S; ++sp) mx = fmaxf(mx, fs.w[tid * S + sp]);
+      fs.mx[tid] = mx;
+    }
+    __syncthreads();
+    for (int idx = tid; idx < cg * S; idx += kThreads) {
+      const int c = idx / S;
+      fs.w[idx] = fs.l[idx] > 0.f ? fast_exp2(fs.w[idx] - fs.mx[c]) : 0.f;
+    }
+    __syncthreads();
+    if (tid < cg) {
+      float dg[kMergeGroups];
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) dg[g] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += kMergeGroups)
+#pragma unroll
+        for (int g = 0; g < kMergeGroups; ++g) {
+          const int sp = s0 + g;
+          if (sp < S) {
+            const float ws = fs.w[tid * S + sp];
+            dg[g] = ws != 0.f ? __builtin_fmaf(ws, fs.l[tid * S + sp], dg[g]) : dg[g];
+          }
+        }
+      float den = 0.f;
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) den += dg[g];
+      fs.den[tid] = den;
+    }
+    __syncthreads();
+    // every partial element of the group
+    for (int idx = tid; idx < cg * HD; idx += kThreads) {
+      const int c = idx / HD, d = idx - c * HD;
+      const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
+      const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+      const float *o = a.part_o + th * S * HD + d;
+      const float *w = fs.w + c * S;
+      float num[kMergeGroups];
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) num[g] = 0.f;
+      for (int s0 = 0; s0 < S; s0 += kMergeGroups) {
+        float v[kMergeGroups];
+#pragma unroll
+        for (int g = 0; g < kMergeGroups; ++g) v[g] = ld(o + static_cast<int64_t>(min(s0 + g, S - 1)) * HD);
+#pragma unroll
+        for (int g = 0; g < kMergeGroups; ++g) {
+          const int sp = s0 + g;
+          if (sp < S) {
+            const float ws = w[sp];
+            num[g] = ws != 0.f ? __builtin_fmaf(ws, v[g], num[g]) : num[g];
+          }
+        }
+      }
+      float n = 0.f;
+#pragma unroll
+      for (int g = 0; g < kMergeGroups; ++g) n += num[g];
+      const float den = fs.den[c];
+      a.out[th * HD + d] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
+    }
+    __syncthreads();
+  }
+  if (tid == 0) __hip_atomic_store(&a.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
 // The running max of a column only moves when a page's max exceeds it by more
@@ -220,7 +426,7 @@ __device__ __forceinline__ Column tile_column(int c, int group, int nrows, int h
 constexpr float kRescaleSlack = 8.f;
 
 template <int HD>
-__global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;   // QK^T MFMA steps (32 hd elements each)
   constexpr int DJ = HD / 16;   // PV MFMA output blocks (16 hd columns each)
   constexpr int VLD = HD / 32;  // 16-byte V loads per lane per page
@@ -230,7 +436,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   __shared__ float xfer[kWaves][16];
   __shared__ int s_is_last;
   static_assert(2 * (16 * HD + 32) * 4 <= kWaves * kPage * VSTR * 2, "merge slots must fit the V staging area");
-  static_assert(sizeof(MergeScratch) <= sizeof(vtile), "merge scratch must fit the V staging area");
+  static_assert(sizeof(FusedScratch) <= sizeof(vtile), "merge scratch must fit the V staging area");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -245,15 +451,8 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   const int kh = b % a.nkv;
   const int t0 = b / a.nkv;
 
-  // ---- tile: rows t0 .. t0+nrows-1 share the origin; t0 must lead it ----
-  // Lane r (< rmax) reads row t0 + r; Q for every possible column is requested
-  // in the same round, before the tile is known.
-  const bool lrow = lane < a.rmax && t0 + lane < a.rows;
-  const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
-  const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
-  const int hi_l = lrow ? a.kv_last[t0 + lane] : -1;
-  const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
-  const Column col0 = tile_column(ln, a.group, a.rmax, hb);  // before the row count is known
+  // ---- tile; Q for every possible column is requested in the same round ----
+  const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
   bf16x8 qop[KJ];
   {
     const bool q_in = col0.on && t0 + col0.row < a.rows;
@@ -268,32 +467,20 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
       }
     }
   }
-  const int origin = __builtin_amdgcn_readfirstlane(org_l);
-  if (t0 % a.rmax != 0 && prev_origin == origin) return;
-  const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != origin || (t0 + lane) % a.rmax == 0));
-  const int nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
-  const int lo_l = a.window > 0 ? max(0, qp_l + 1 - a.window) : 0;
-  const bool live = lane < nrows && hi_l >= lo_l;
-  int lo_min = live ? lo_l : INT_MAX, hi_max = live ? hi_l : -1;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    lo_min = min(lo_min, __shfl_xor(lo_min, off));
-    hi_max = max(hi_max, __shfl_xor(hi_max, off));
-  }
-  lo_min = __builtin_amdgcn_readfirstlane(lo_min);
-  hi_max = __builtin_amdgcn_readfirstlane(hi_max);
-  int pbeg = 0, pend = 0;
-  if (hi_max >= 0) {
-    const int p0 = lo_min / kPage;
-    const int64_t npg = hi_max / kPage - p0 + 1;
-    pbeg = p0 + static_cast<int>(npg * split / a.splits);
-    pend = p0 + static_cast<int>(npg * (split + 1) / a.splits);
-  }
+  const Tile tile = tile_rows(a, t0, lane);
+  if (!tile.lead) return;
+  const int origin = tile.origin;
+  const int nrows = tile.nrows;
+  const int lo_l = tile.lo_l, hi_l = tile.hi_l;
+  int pbeg, pend;
+  split_range(tile, split, a.splits, pbeg, pend);
 
   // ---- this lane's score column ----
-  const Column col = tile_column(ln, a.group, nrows, hb);
+  const Column col = tile_column(ln, a.group, nrows, hb, 16);
   const int col_lo = __shfl(lo_l, col.row);
-  const int col_hi = col.on ? __shfl(hi_l, col.row) : -1;
+  // shuffle with every lane active, then drop columns without a row
+  const int col_hi_any = __shfl(hi_l, col.row);
+  const int col_hi = col.on ? col_hi_any : -1;
   if (!col.on) {
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
@@ -353,38 +540,44 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   };
   auto compute_page = [&](int k, const bf16x8(&kop)[KJ], const u32x4(&vreg)[VLD]) {
     const int p = first + kWaves * k;
-    // Visibility of the 4 tokens this lane scores, and of each token for any column.
+    // Pages every row sees in full need no per-token masks (columns without a
+    // row hold Q = 0 and are never written out).
+    const bool full = p >= tile.fp0 && p < tile.fp1;
     const int pos0 = p * kPage + 4 * lc;
-    bool vis[4];
-    uint32_t tokmask = 0;
+    bool vis[4] = {true, true, true, true};
+    uint32_t tokmask = 0xffffu;
+    if (!full) {
+      tokmask = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      vis[i] = col.on && pos0 + i >= col_lo && pos0 + i <= col_hi;
-      const uint64_t bal = __ballot(vis[i]);
+      for (int i = 0; i < 4; ++i) {
+        vis[i] = col.on && pos0 + i >= col_lo && pos0 + i <= col_hi;
+        const uint64_t bal = __ballot(vis[i]);
 #pragma unroll
-      for (int g = 0; g < 4; ++g)
-        if ((bal >> (16 * g)) & 0xffffull) tokmask |= 1u << (4 * g + i);
+        for (int g = 0; g < 4; ++g)
+          if ((bal >> (16 * g)) & 0xffffull) tokmask |= 1u << (4 * g + i);
+      }
+      if (tokmask == 0) return;
     }
-    if (tokmask == 0) return;
 
     // S^T: lane holds scores of tokens 4*lc+i for column ln.
     f32x4 sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < KJ; ++j) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[j], qop[j], sc, 0, 0, 0);
 
-    float s2[4];
+    float sv[4];
     float mx = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      s2[i] = vis[i] ? sc[i] * kLog2e : -INFINITY;
-      mx = fmaxf(mx, s2[i]);
+      sv[i] = vis[i] ? sc[i] : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
     }
     mx = fmaxf(mx, __shfl_xor(mx, 16));
     mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = mx * kLog2e;
     // Move the reference max only when this page exceeds it by the slack.
-    const bool grow = mx > m_run + kRescaleSlack;
+    const bool grow = m2 > m_run + kRescaleSlack;
     if (__ballot(grow) != 0) {
-      const float m_new = grow ? mx : m_run;
+      const float m_new = grow ? m2 : m_run;
       const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
       m_run = m_new;
       // factors move from the column layout (lane ln) to the output layout
@@ -396,12 +589,13 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
       for (int jj = 0; jj < DJ; ++jj) oacc[jj] *= al;
       lacc *= al;
     }
-    s16x4 pa;
+    float pr[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const float pr = vis[i] ? fast_exp2(s2[i] - m_run) : 0.f;
-      pa[i] = static_cast<short>(f32_to_bf16_rne(pr));
+      pr[i] = fast_exp2(__builtin_fmaf(sv[i], kLog2e, -m_run));
+      if (!full) pr[i] = sv[i] == -INFINITY ? 0.f : pr[i];
     }
+    const s16x4 pa = pack_weights(pr[0], pr[1], pr[2], pr[3]);
 
     // Stage V; tokens no column can see are zeroed (they may hold NaN).
 #pragma unroll
@@ -409,7 +603,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
       const int e = (j * 64 + lane) * 8;
       const int tok = e / HD;
       u32x4 v = vreg[j];
-      if (!((tokmask >> tok) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
+      if (!full && !((tokmask >> tok) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
       *reinterpret_cast<u32x4 *>(vt + tok * VSTR + (e - tok * HD)) = v;
     }
     wave_lds_sync();
@@ -506,7 +700,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
     for (int i = 0; i < 4; ++i) {
       const int r = 4 * lc + i;
       if (r >= ncols) continue;
-      const Column rc = tile_column(r, a.group, nrows, hb);
+      const Column rc = tile_column(r, a.group, nrows, hb, 16);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
       if (a.splits == 1) {
         const float l = lacc[i];
@@ -538,27 +732,318 @@ __global__ __launch_bounds__(kThreads) void pgqa_split_kernel(DecodeArgs a) {
   }
   if (!fused) return;
 
-  // ---- fused merge: the last workgroup of this unit merges every split ----
-  wait_all_memory();  // this workgroup's partial stores have completed
-  __syncthreads();
-  const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
-  if (threadIdx.x == 0) {
-    const int prev = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    s_is_last = prev == a.splits - 1;
+  fused_merge<HD>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch *>(&vtile[0][0]), &s_is_last);
+}
+
+// ---------------------------------------------------------------------------
+// Shared-page kernel: tiles of up to 64 columns (e.g. 8 rows x 8 heads of one
+// sequence) and every hd-512 tile.  The 4 waves stage each page's K and V in
+// LDS together with direct-to-LDS loads (global_load_lds_dwordx4) into a ring
+// of page buffers, NBUF-1 pages ahead of the page being computed.
+//   LDS K layout: MFMA operand order -- 16-byte chunk s is the A operand of
+//     step s / 64 for lane s % 64 (token s % 16, hd (4 (s/64) + (s/16) % 4) * 8).
+//   LDS V layout: [hd block of 16][token][16] -- the 16 lanes of a transpose
+//     read group cover 4 tokens x 16 columns contiguously.
+// The waves form 4/NSL column blocks x NSL hd slices: wave w scores column
+// block w / NSL over hd slice w % NSL; with NSL > 1 the slices' partial scores
+// are summed through LDS in slice order, so the waves of a block hold
+// identical scores and softmax state, and each accumulates P V for its own
+// slice.  NSL is fixed per launch (from the widest tile the shapes allow), so
+// every MFMA is unconditional.
+// Every wave waits for its own loads of a page, then a barrier makes the page
+// complete; the same barrier tells that the buffer refilled next is free.
+// ---------------------------------------------------------------------------
+template <int HD, int NSL>
+__global__ __launch_bounds__(kThreads) void pgqa_shared_kernel(DecodeArgs a) {
+  constexpr int KJ = HD / 32;              // QK^T MFMA steps over the whole hd
+  constexpr int DJ = HD / 16;              // PV MFMA output blocks over the whole hd
+  constexpr int KS = KJ / NSL;             // ... per slice
+  constexpr int DS = DJ / NSL;
+  constexpr int QBM = kWaves / NSL;        // column blocks per workgroup
+  constexpr int CAP = 16 * QBM;            // columns per tile
+  // LDS page buffers (separate objects, see below): four, three at hd 512
+  // (32 KB pages).
+  constexpr int NBUF = HD == 512 ? 3 : 4;
+  constexpr int PAGE_ELEMS = kPage * HD;   // bf16 elements of one K (or V) page
+  constexpr int LW = HD / 128;             // 1 KB direct loads per wave per page, each of K and V
+  constexpr int INFLIGHT = (NBUF - 2) * 2 * LW;  // this wave's loads still allowed in flight
+  static_assert(LW >= 1 && KS >= 1, "the shared-page kernel needs hd >= 128 and hd / 32 >= slices");
+  // One object per ring buffer and a page loop unrolled by NBUF, so every LDS
+  // access names its buffer at compile time and the compiler can tell reads
+  // of one buffer from the direct loads still landing in the others.
+  __shared__ __attribute__((aligned(16))) uint16_t stage0[2 * PAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stage1[2 * PAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stage2[2 * PAGE_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t stage3[NBUF > 3 ? 2 * PAGE_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) f32x4 xscore[kWaves][64];  // partial scores per wave
+  __shared__ float xfer[kWaves][16];
+  __shared__ int s_is_last;
+  static_assert(sizeof(FusedScratch) <= sizeof(stage0), "merge scratch must fit a staging buffer");
+  uint16_t *const stage_ptr[4] = {stage0, stage1, stage2, stage3};
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int ln = lane & 15;
+  const int lc = lane >> 4;
+  const int cb = wave / NSL;  // this wave's column block
+  const int sl = wave % NSL;  // ... and hd slice
+  const int j0 = sl * KS;     // first QK step of the slice
+  const int jj0 = sl * DS;    // first PV block of the slice
+
+  int b = blockIdx.x;
+  const int split = b % a.splits;
+  b /= a.splits;
+  const int hb = b % a.hblocks;
+  b /= a.hblocks;
+  const int kh = b % a.nkv;
+  const int t0 = b / a.nkv;
+
+  const Tile tile = tile_rows(a, t0, lane);
+  if (!tile.lead) return;
+  const int nrows = tile.nrows;
+  int pbeg, pend;
+  split_range(tile, split, a.splits, pbeg, pend);
+  const int ncols = a.group <= CAP ? nrows * a.group : min(CAP, a.group - hb * CAP);
+  const bool active = 16 * cb < ncols;  // this wave's column block exists (wave-uniform)
+
+  const Column col = tile_column(16 * cb + ln, a.group, nrows, hb, CAP);
+  const int col_lo = __shfl(tile.lo_l, col.row);
+  // shuffle with every lane active, then drop columns without a row
+  const int col_hi_any = __shfl(tile.hi_l, col.row);
+  const int col_hi = col.on ? col_hi_any : -1;
+  bf16x8 qop[KS];
+  {
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (col.on ? col.row : 0)) * a.nh + kh * a.group + col.head) * HD;
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qop[u] = __builtin_bit_cast(bf16x8, z);
+      if (col.on) qop[u] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * (j0 + u) + lc) * 8);
+    }
   }
-  __syncthreads();
-  if (!s_is_last) return;
-  MergeScratch &ms = *reinterpret_cast<MergeScratch *>(&vtile[0][0]);
-  for (int c = 0; c < ncols; ++c) {
-    const Column rc = tile_column(c, a.group, nrows, hb);
-    const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-    const float den = merge_weights(LoadCoherent{}, a.part_ml + th * a.splits * 2, a.splits, ms);
-#pragma unroll 1
-    for (int d0 = 0; d0 < HD; d0 += kMergeChunk)
-      merge_chunk<(HD < kMergeChunk ? HD : kMergeChunk) / 32>(LoadCoherent{}, a.part_o + th * a.splits * HD, a.splits, HD, d0,
-                                                               den, ms, a.out + th * HD);
+
+  float m_run = -INFINITY;
+  f32x4 oacc[DS];
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < DS; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const s16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
+  const int64_t kv_head_off = static_cast<int64_t>(kh) * kPage * HD;
+  const int64_t page_elems = static_cast<int64_t>(a.nkv) * kPage * HD;
+
+  // Global source (element offset in the page) of this lane's chunk of each
+  // of the wave's 1 KB direct loads: K chunk s = 64 i + lane, V chunk likewise.
+  int k_src[LW], v_src[LW];
+#pragma unroll
+  for (int r = 0; r < LW; ++r) {
+    const int s = (wave * LW + r) * 64 + lane;
+    k_src[r] = (s & 15) * HD + (4 * (s >> 6) + ((s >> 4) & 3)) * 8;
+    v_src[r] = ((s & 31) >> 1) * HD + (s >> 5) * 16 + (s & 1) * 8;
   }
-  if (threadIdx.x == 0) __hip_atomic_store(&a.counters[unit], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+
+  const int nk = pend - pbeg;
+  int pv0 = 0, pv1 = 0, pw0 = -1;  // physical pages of pages [pw0, pw0 + 128)
+  auto fetch_window = [&](int w0) {
+    int ph[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = w0 + 64 * h + lane;
+      ph[h] = 0;
+      if (k < nk) {
+        ph[h] = a.block_table[tile.origin + pbeg + k];
+        if (a.page_map) ph[h] = a.page_map[ph[h]];
+      }
+    }
+    pv0 = ph[0];
+    pv1 = ph[1];
+    pw0 = w0;
+    wait_all_memory();
+  };
+  // Requests page k (clamped to the last page) into ring buffer dst.
+  auto issue_page = [&](int k, uint16_t *dst) {
+    k = min(k, nk - 1);
+    if (k - pw0 >= 128) fetch_window(k);  // drains the ring once per 128 pages
+    const int kw = k - pw0;
+    const int phys = kw < 64 ? __builtin_amdgcn_readlane(pv0, kw) : __builtin_amdgcn_readlane(pv1, kw - 64);
+    const int64_t page_off = static_cast<int64_t>(phys) * page_elems + kv_head_off;
+    const uint16_t *kp = a.k_pool + page_off;
+    const uint16_t *vp = a.v_pool + page_off;
+    uint16_t *kdst = dst + wave * LW * 512;
+    uint16_t *vdst = dst + PAGE_ELEMS + wave * LW * 512;
+#pragma unroll
+    for (int r = 0; r < LW; ++r) {
+      load_to_lds16(kp + k_src[r], kdst + r * 512);
+      load_to_lds16(vp + v_src[r], vdst + r * 512);
+    }
+  };
+
+  // One page: wait for it, refill the buffer of the page before it, compute it.
+  auto step = [&](int k, const uint16_t *kt, uint16_t *refill) {
+    // this wave's loads of page k have landed once at most the newer pages'
+    // loads are outstanding; the barrier then makes the whole page visible and
+    // tells that the buffer of page k - 1 is no longer read
+    __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0f70);
+    lds_barrier();
+    issue_page(k + NBUF - 1, refill);
+    if (k >= nk) return;
+
+    const int p = pbeg + k;
+    const bool full = p >= tile.fp0 && p < tile.fp1;  // the same in every wave
+    uint32_t tokmask = 0xffffu;
+    if (!full) {
+      // tokens of this page some row of the tile can see
+      uint32_t mrow = 0;
+      if (lane < nrows) {
+        const int lo = max(tile.lo_l - p * kPage, 0), hi = min(tile.hi_l - p * kPage, kPage - 1);
+        if (hi >= lo) mrow = ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+      }
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) mrow |= __shfl_xor(mrow, off);
+      tokmask = __builtin_amdgcn_readfirstlane(mrow);
+    }
+    if (tokmask == 0) return;  // the same in every wave
+
+    const uint16_t *vt = kt + PAGE_ELEMS;
+    // partial scores over this wave's hd slice: all K operands read first,
+    // two accumulation chains
+    bf16x8 kop[KS];
+#pragma unroll
+    for (int u = 0; u < KS; ++u) kop[u] = *reinterpret_cast<const bf16x8 *>(kt + ((j0 + u) * 64 + lane) * 8);
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int u = 0; u < KS; ++u) {
+      if ((u & 1) == 0) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc, 0, 0, 0);
+      else sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc1, 0, 0, 0);
+    }
+    if constexpr (KS > 1) sc += sc1;
+    if constexpr (NSL > 1) {
+      xscore[wave][lane] = sc;
+      lds_barrier();
+      sc = xscore[cb * NSL][lane];
+#pragma unroll
+      for (int s2 = 1; s2 < NSL; ++s2) sc += xscore[cb * NSL + s2][lane];
+    }
+    if (!active) return;
+
+    bool vis[4] = {true, true, true, true};
+    if (!full) {
+      const int pos0 = p * kPage + 4 * lc;
+#pragma unroll
+      for (int t = 0; t < 4; ++t) vis[t] = pos0 + t >= col_lo && pos0 + t <= col_hi;
+    }
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      sv[t] = vis[t] ? sc[t] : -INFINITY;
+      mx = fmaxf(mx, sv[t]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = mx * kLog2e;
+    const bool grow = m2 > m_run + kRescaleSlack;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? m2 : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      if (lc == 0) xfer[wave][ln] = alpha;
+      wave_lds_sync();
+      const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+#pragma unroll
+      for (int u = 0; u < DS; ++u) oacc[u] *= al;
+      lacc *= al;
+    }
+    float pr[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      pr[t] = fast_exp2(__builtin_fmaf(sv[t], kLog2e, -m_run));
+      if (!full) pr[t] = sv[t] == -INFINITY ? 0.f : pr[t];
+    }
+    const s16x4 pa = pack_weights(pr[0], pr[1], pr[2], pr[3]);
+    // lane (4m+q) of group lc reads token 4 lc + m, columns 4q..4q+3 of each block
+    const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * 16 + 4 * (ln & 3) + jj0 * 256;
+    // tokens no column can see may hold NaN: zero their V entries (slow path)
+    const uint32_t keep = (tokmask >> (4 * lc)) & 0xfu;
+    s16x4 vb[DS];
+#pragma unroll
+    for (int u = 0; u < DS; ++u)
+      vb[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(vtr + u * 256));
+#pragma unroll
+    for (int u = 0; u < DS; ++u) {
+      if (!full) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) vb[u][r] = (keep >> r) & 1u ? vb[u][r] : static_cast<short>(0);
+      }
+      oacc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[u], oacc[u], 0, 0, 0);
+    }
+    lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
+  };
+
+  if (nk > 0) {
+    fetch_window(0);
+#pragma unroll
+    for (int i = 0; i < NBUF - 1; ++i) issue_page(i, stage_ptr[i]);
+    if constexpr (NBUF == 4) {
+      for (int k = 0; k < nk; k += 4) {
+        step(k, stage_ptr[0], stage_ptr[3]);
+        step(k + 1, stage_ptr[1], stage_ptr[0]);
+        step(k + 2, stage_ptr[2], stage_ptr[1]);
+        step(k + 3, stage_ptr[3], stage_ptr[2]);
+      }
+    } else {
+      for (int k = 0; k < nk; k += 3) {
+        step(k, stage_ptr[0], stage_ptr[2]);
+        step(k + 1, stage_ptr[1], stage_ptr[0]);
+        step(k + 2, stage_ptr[2], stage_ptr[1]);
+      }
+    }
+  }
+  wait_all_memory();  // the ring's trailing (repeated) loads have landed
+  __syncthreads();
+
+  // ---- results: this wave's hd slice of its column block ----
+  const bool fused = a.splits > 1 && a.counters != nullptr;
+  if (active) {
+    if (lc == 0) xfer[wave][ln] = m_run;
+    wave_lds_sync();
+    const f32x4 mo = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int r = 16 * cb + 4 * lc + i;
+      if (r >= ncols) continue;
+      const Column rc = tile_column(r, a.group, nrows, hb, CAP);
+      const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+      if (a.splits == 1) {
+        const float l = lacc[i];
+#pragma unroll
+        for (int u = 0; u < DS; ++u) {
+          const float v = l > 0.f ? oacc[u][i] / l : 0.f;
+          a.out[th * HD + 16 * (jj0 + u) + ln] = f32_to_bf16_rne(v);
+        }
+      } else {
+        const int64_t ps = th * a.splits + split;
+        float *po = a.part_o + ps * HD + 16 * jj0;
+        if (fused) {
+#pragma unroll
+          for (int u = 0; u < DS; ++u) store_coherent(po + 16 * u + ln, oacc[u][i]);
+          if (sl == 0 && ln == 0) {
+            store_coherent(a.part_ml + 2 * ps, mo[i]);
+            store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
+          }
+        } else {
+#pragma unroll
+          for (int u = 0; u < DS; ++u) po[16 * u + ln] = oacc[u][i];
+          if (sl == 0 && ln == 0) {
+            a.part_ml[2 * ps] = mo[i];
+            a.part_ml[2 * ps + 1] = lacc[i];
+          }
+        }
+      }
+    }
+  }
+  if (!fused) return;
+  fused_merge<HD>(a, t0, kh, hb, nrows, ncols, CAP, reinterpret_cast<FusedScratch *>(stage_ptr[0]), &s_is_last);
 }
 
 // Separate merge: one workgroup per (row, query head, chunk of hd).
@@ -583,10 +1068,50 @@ int fail(int code, const char *fmt, ...) {
   return code;
 }
 
+// Which kernel runs and how rows are tiled, from the call's shapes only (so
+// calls that differ only in data -- merge mode, page placement -- run the same
+// code).  The shared-page kernel takes hd 512 and, from hd 128 up, tiles of
+// more than 16 columns; the per-wave kernel the rest.  With fewer columns than
+// the shared-page kernel's 64 the hd is cut into slices so that all 4 waves
+// still have work.
+struct Plan {
+  int kind;     // 0: per-wave kernel, 1: shared-page kernel
+  int nsl;      // hd slices per column block (shared-page kernel)
+  int cap;      // columns per tile
+  int rmax;     // rows per tile
+  int hblocks;  // head blocks per kv head
+};
+Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
+  Plan p;
+  const int64_t cols = group <= 64 ? group * (rows < 64 / group ? rows : 64 / group) : 64;
+  // groups of 8+ heads: several rows of one sequence fill a 64-column tile
+  // (multi-row decode); narrower groups keep the per-wave kernel, whose
+  // 16-column tiles waste nothing when every row has its own sequence
+  p.kind = hd == 512 || (hd >= 128 && cols > 16 && group >= 8) ? 1 : 0;
+  p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
+  if (p.kind == 1 && hd == 128 && p.nsl == 4) p.nsl = 2;  // hd 128 has 4 QK steps
+  p.cap = p.kind == 1 ? 16 * (kWaves / p.nsl) : 16;
+  p.rmax = group <= p.cap ? static_cast<int>(p.cap / group) : 1;
+  p.hblocks = group <= p.cap ? 1 : static_cast<int>((group + p.cap - 1) / p.cap);
+  return p;
+}
+
 template <int HD>
-hipError_t launch_decode(const DecodeArgs &a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL(pgqa_split_kernel<HD>, dim3(static_cast<unsigned>(blocks)), dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
+  if constexpr (HD >= 128) {
+    if (p.kind == 1) {
+      if (p.nsl == 1) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 1>), grid, block, 0, stream, a);
+      else if (p.nsl == 2) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 2>), grid, block, 0, stream, a);
+      else if constexpr (HD >= 256) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 4>), grid, block, 0, stream, a);
+      return hipGetLastError();
+    }
+  }
+  if constexpr (HD < 512) {
+    hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
+    return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
@@ -643,11 +1168,12 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(PGQA_EINVAL, "out must be 2-byte aligned");
 
   const int64_t group = nh / nkv;
-  const int64_t hblocks = group <= 16 ? 1 : (group + 15) / 16;
-  const int64_t rmax = group <= 16 ? 16 / group : 1;
-  const int64_t units = rows * nkv * hblocks;
-  if (counters && splits > 1 && units > kCounterCap)
-    return fail(PGQA_ECAP, "%lld merge units exceed the %d counters", (long long)units, kCounterCap);
+  const Plan plan = make_plan(rows, group, hd);
+  const int64_t units = rows * nkv * plan.hblocks;
+  // the documented (kernel-independent) bound: at most rows * nkv * ceil(group / 16) units
+  if (counters && splits > 1 && rows * nkv * ((group + 15) / 16) > kCounterCap)
+    return fail(PGQA_ECAP, "rows * nkv * ceil(group / 16) = %lld exceeds the %d counters",
+                (long long)(rows * nkv * ((group + 15) / 16)), kCounterCap);
   if (rows * nh * (hd > 128 ? hd / 128 : 1) > INT_MAX) return fail(PGQA_EINVAL, "rows * nh too large");
   const int64_t blocks = units * splits;
   if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
@@ -671,16 +1197,17 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   a.group = static_cast<int>(group);
   a.window = static_cast<int>(window);
   a.splits = static_cast<int>(splits);
-  a.rmax = static_cast<int>(rmax);
-  a.hblocks = static_cast<int>(hblocks);
+  a.rmax = plan.rmax;
+  a.hblocks = plan.hblocks;
+  a.cap = plan.cap;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   switch (hd) {
-    case 64: err = launch_decode<64>(a, blocks, st); break;
-    case 128: err = launch_decode<128>(a, blocks, st); break;
-    case 256: err = launch_decode<256>(a, blocks, st); break;
-    default: err = launch_decode<512>(a, blocks, st); break;
+    case 64: err = launch_decode<64>(a, plan, blocks, st); break;
+    case 128: err = launch_decode<128>(a, plan, blocks, st); break;
+    case 256: err = launch_decode<256>(a, plan, blocks, st); break;
+    default: err = launch_decode<512>(a, plan, blocks, st); break;
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {

@@ -157,6 +157,13 @@ def edge_workloads():
     # rows whose last visible key is below the query position (second position array)
     w2 = rng_seq("kvlast", ctx=500, rows=4, nh=8, nkv=2, hd=256, window=0)
     cases.append(w2.replace(name="kvlast", kv_last=np.array([100, 499, 300, 498], np.int32)))
+    # shared-page kernel shapes: hd split in 2 slices (group 8, 3 rows, hd 128);
+    # 64-column tiles with a ragged last tile (group 16, 5 rows; hd 512, 9 rows);
+    # a group wider than a tile (128 heads -> two head blocks of 64)
+    cases.append(rng_seq("sh128s2", ctx=300, rows=3, nh=16, nkv=2, hd=128, window=0))
+    cases.append(rng_seq("sh128s1", ctx=400, rows=5, nh=16, nkv=1, hd=128, window=77))
+    cases.append(rng_seq("sh512s1", ctx=150, rows=9, nh=8, nkv=1, hd=512, window=0))
+    cases.append(rng_seq("sh256g128", ctx=260, rows=2, nh=128, nkv=1, hd=256, window=0))
     # an empty visible set (last key below the window start) -> zeros
     w3 = rng_seq("empty", ctx=200, rows=2, nh=4, nkv=1, hd=64, window=8)
     cases.append(w3.replace(name="empty", kv_last=np.array([150, 199], np.int32)))
