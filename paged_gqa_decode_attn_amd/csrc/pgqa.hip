@@ -1124,11 +1124,13 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
   const int64_t units = nseq * nkv;
   const int64_t pages = (kv_span + kPage - 1) / kPage;
-  // Aim at two 4-wave workgroups per CU on the 256 CUs, with at least 8 pages
-  // (2 per wave) in every split.
-  const int64_t target = 512;
+  // Aim at about 8 workgroups per CU on the 256 CUs (uneven sequence lengths
+  // then still balance), with at least 16 pages in a split of a long span and
+  // up to 8 splits of at least 4 pages for a short one.
+  const int64_t target = 2048;
   int64_t s = (target + units - 1) / units;
-  int64_t smax = pages / 8;
+  int64_t smax = pages / 4 < 8 ? pages / 4 : 8;
+  if (pages / 16 > smax) smax = pages / 16;
   if (smax < 1) smax = 1;
   if (smax > kMaxSplits) smax = kMaxSplits;
   if (s > smax) s = smax;
