@@ -99,7 +99,14 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     counters = torch.zeros(pg.counter_capacity(), dtype=torch.int32, device="cuda") if mode == "fused" else None
     out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
     part = torch.empty(max(1, pg.decode_part_bytes(w.rows, w.nh, splits, w.hd)), dtype=torch.uint8, device="cuda")
-    scratch = torch.empty(1 << 30, dtype=torch.uint8, device="cuda") if flush else None
+    # Cache eviction between timed steps: "read" streams a 1 GiB buffer (L2 and
+    # the 256 MB Infinity Cache end up holding clean lines of it), "rw" also
+    # writes it (the caches then hold dirty lines that the next step must write
+    # back to HBM while it runs).
+    if flush is True:
+        flush = "read"
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if flush else None
+    sink = torch.zeros((), dtype=torch.int64, device="cuda") if flush else None
     stream = torch.cuda.current_stream()
 
     def step():
@@ -112,8 +119,10 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
-        if scratch is not None:
-            scratch.add_(1)  # evicts L2 and the Infinity Cache between steps
+        if flush == "read":
+            torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+        elif flush == "rw":
+            scratch.add_(1)
         ev[i][0].record(stream)
         step()
         ev[i][1].record(stream)

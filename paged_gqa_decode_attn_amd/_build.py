@@ -10,7 +10,7 @@ INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++20", "-fPIC", "-shared",
     "-Wall", "-Wno-unused-command-line-argument",
     # packed-FP32 VALU ops stay off (device side; the host pass ignores it)
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",

@@ -40,6 +40,7 @@
 #include <cstdio>
 #include <cstring>
 #include <type_traits>
+#include <utility>
 
 #include "pgqa.h"
 
@@ -88,6 +89,24 @@ __device__ __forceinline__ void load_to_lds16(const void *src, void *lds_base) {
   __builtin_amdgcn_global_load_lds(src, (__attribute__((address_space(3))) void *)lds_base, 16, 0, 0);
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16) of a tile that direct-to-LDS loads
+// filled: within each 16-lane group, lane i receives elements i, i+16, i+32 and
+// i+48 of the group's concatenated 8-byte rows.  Written as inline assembly
+// because the compiler's own form of this read carries no record of which LDS
+// object it reads, so the compiler would wait for every direct load still in
+// flight (the whole prefetch ring) before it; here the caller waits instead:
+// results are valid only after lds_wait_reads().
+template <int OFFSET>
+__device__ __forceinline__ s16x4 lds_read_tr16(uint32_t lds_addr) {
+  s16x4 r;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(r) : "v"(lds_addr), "i"(OFFSET));
+  return r;
+}
+__device__ __forceinline__ void lds_wait_reads() { asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory"); }
+__device__ __forceinline__ uint32_t lds_address(const void *p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const void *)p));
+}
+
 // Workgroup barrier for LDS exchanges only: waits for this wave's LDS traffic,
 // not for its vector-memory loads (which stay in flight across it).
 __device__ __forceinline__ void lds_barrier() {
@@ -117,17 +136,15 @@ __device__ __forceinline__ s16x4 pack_weights(float p0, float p1, float p2, floa
                static_cast<short>(u1 >> 16)};
 }
 
-// Agent-coherent 32-bit accesses for data exchanged between workgroups inside
-// one launch (the fused merge).  They go past this XCD's L2, so no L2
-// write-back fence is needed; ordering comes from waiting for the stores to
-// complete before the counter ticket, and from the ticket's result gating the
-// loads.
+// Agent-coherent 32-bit accesses for the partial results.  The stores go past
+// this XCD's L2 (write-through), so the fused merge needs no L2 write-back
+// fence -- its ordering comes from waiting for the stores to complete before
+// the counter ticket, and from the ticket's result gating the loads -- and a
+// launch that leaves its partials for the combine kernel ends without
+// megabytes of dirty L2 lines to write back.
 __device__ __forceinline__ void store_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-struct LoadPlain {
-  __device__ __forceinline__ float operator()(const float *p) const { return *p; }
-};
 struct LoadCoherent {
   __device__ __forceinline__ float operator()(const float *p) const {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -141,106 +158,20 @@ __device__ __forceinline__ void wait_all_memory() { __builtin_amdgcn_s_waitcnt(0
 //   num = sum_g ( sum_{s = g mod 8, s ascending} w_s o_s[d] ),  g = 0..7 in order
 //   den = the same grouping over w_s l_s,  out = num / den  (0 if den == 0).
 // The eight strided groups let the loads of a merge run in parallel; the order
-// is fixed, and both the fused last-workgroup merge and the combine kernel run
-// this exact code (they differ only in how the partials are loaded), so the
-// two paths give the same bits.
+// is fixed, and both the fused last-workgroup merge and the combine kernel
+// take exactly these steps per output element, so the two paths give the same
+// bits.
 constexpr int kMergeGroups = 8;
-constexpr int kMergeChunk = 128;  // hd elements merged per pass
 
-// LDS scratch of a merge: split weights, split sums, reductions, group sums.
-struct MergeScratch {
-  float w[kMaxSplits];
-  float l[kMaxSplits];
-  float red[16];
-  float acc[kMergeGroups][kMergeChunk];
-};
-
-// LDS scratch of the fused merge: weights and sums of up to kThreads
-// (column, split) pairs, per-column max and denominator.
+// LDS scratch of the fused merge: weights and sums of up to NT (column,
+// split) pairs, per-column max and denominator (NT = workgroup size).
+template <int NT>
 struct FusedScratch {
-  float w[kThreads];
-  float l[kThreads];
-  float mx[kThreads];
-  float den[kThreads];
+  float w[NT];
+  float l[NT];
+  float mx[NT];
+  float den[NT];
 };
-
-// Fills ms.w / ms.l for one (row, head) and returns the denominator.  Every
-// thread of the (256-thread) workgroup calls it.
-template <class Load>
-__device__ float merge_weights(Load ld, const float *ml, int splits, MergeScratch &ms) {
-  const int tid = threadIdx.x;
-  float m = -INFINITY, l = 0.f;
-  if (tid < splits) {
-    const float mm = ld(ml + 2 * tid);
-    l = ld(ml + 2 * tid + 1);
-    if (l > 0.f) m = mm;
-  }
-  float mx = m;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) ms.red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(ms.red[0], ms.red[1]), fmaxf(ms.red[2], ms.red[3]));
-  ms.w[tid] = (tid < splits && l > 0.f) ? fast_exp2(m - mx) : 0.f;
-  ms.l[tid] = l;
-  __syncthreads();
-  if (tid < kMergeGroups) {
-    float dg = 0.f;
-    for (int s = tid; s < splits; s += kMergeGroups) {
-      const float ws = ms.w[s];
-      dg = ws != 0.f ? __builtin_fmaf(ws, ms.l[s], dg) : dg;
-    }
-    ms.red[8 + tid] = dg;
-  }
-  __syncthreads();
-  float den = 0.f;
-#pragma unroll
-  for (int g = 0; g < kMergeGroups; ++g) den += ms.red[8 + g];
-  return den;
-}
-
-// Merges hd elements d0 .. d0 + 32*NB - 1 of one (row, head) and writes them
-// as bf16 to out_row[d].  Thread (g, e) = (tid / 32, tid % 32) accumulates
-// group g for elements d0 + 32*b + e.
-template <int NB, class Load>
-__device__ void merge_chunk(Load ld, const float *o, int splits, int hd, int d0, float den, MergeScratch &ms,
-                            uint16_t *out_row) {
-  const int tid = threadIdx.x;
-  const int g = tid >> 5, e = tid & 31;
-  float num[NB];
-#pragma unroll
-  for (int b = 0; b < NB; ++b) num[b] = 0.f;
-  // 4 splits of this group per step, all loads issued before any is used
-  for (int s = g; s < splits; s += 4 * kMergeGroups) {
-    float v[4][NB];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int su = min(s + u * kMergeGroups, splits - 1);
-      const float *os = o + static_cast<int64_t>(su) * hd + d0 + e;
-#pragma unroll
-      for (int b = 0; b < NB; ++b) v[u][b] = ld(os + 32 * b);
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int su = s + u * kMergeGroups;
-      if (su < splits) {
-        const float ws = ms.w[su];
-#pragma unroll
-        for (int b = 0; b < NB; ++b) num[b] = ws != 0.f ? __builtin_fmaf(ws, v[u][b], num[b]) : num[b];
-      }
-    }
-  }
-#pragma unroll
-  for (int b = 0; b < NB; ++b) ms.acc[g][32 * b + e] = num[b];
-  __syncthreads();
-  if (tid < 32 * NB) {
-    float n = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < kMergeGroups; ++gg) n += ms.acc[gg][tid];
-    out_row[d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
-  }
-  __syncthreads();
-}
 
 // Column c (0 .. cap-1) of a tile -> (row offset, head within the kv group),
 // or off if the tile has no such column.  A group of at most `cap` heads keeps
@@ -322,13 +253,13 @@ __device__ __forceinline__ void split_range(const Tile &t, int split, int splits
 // ---- fused merge: the last workgroup of a merge unit merges every split ----
 // Called by all threads once this workgroup's partial stores are issued.  The
 // unit's counter is a ticket: the workgroup that draws splits-1 merges and
-// resets the counter to zero.  Columns are taken CG at a time (CG * S <= 256):
+// resets the counter to zero.  Columns are taken CG at a time (CG * S <= NT):
 // one round of loads fetches every (m, l) of the group, a second every partial
 // element; each thread keeps the eight group sums of its elements, which is
 // the combine kernel's arithmetic element for element.
-template <int HD>
+template <int HD, int NT>
 __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
-                            FusedScratch *fsp, int *s_is_last) {
+                            FusedScratch<NT> *fsp, int *s_is_last) {
   wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
   const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
@@ -338,15 +269,15 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
   }
   __syncthreads();
   if (!*s_is_last) return;
-  FusedScratch &fs = *fsp;
+  FusedScratch<NT> &fs = *fsp;
   const LoadCoherent ld;
   const int S = a.splits;
   const int tid = threadIdx.x;
-  const int cg_max = max(1, min(ncols, kThreads / S));
+  const int cg_max = max(1, min(ncols, NT / S));
   for (int c0 = 0; c0 < ncols; c0 += cg_max) {
     const int cg = min(cg_max, ncols - c0);
     // (m, l) of every (column, split) of the group
-    for (int idx = tid; idx < cg * S; idx += kThreads) {
+    for (int idx = tid; idx < cg * S; idx += NT) {
       const int c = idx / S, sp = idx - c * S;
       const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
@@ -362,7 +293,7 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
       fs.mx[tid] = mx;
     }
     __syncthreads();
-    for (int idx = tid; idx < cg * S; idx += kThreads) {
+    for (int idx = tid; idx < cg * S; idx += NT) {
       const int c = idx / S;
       fs.w[idx] = fs.l[idx] > 0.f ? fast_exp2(fs.w[idx] - fs.mx[c]) : 0.f;
     }
@@ -387,7 +318,7 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
     }
     __syncthreads();
     // every partial element of the group
-    for (int idx = tid; idx < cg * HD; idx += kThreads) {
+    for (int idx = tid; idx < cg * HD; idx += NT) {
       const int c = idx / HD, d = idx - c * HD;
       const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
@@ -436,7 +367,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   __shared__ float xfer[kWaves][16];
   __shared__ int s_is_last;
   static_assert(2 * (16 * HD + 32) * 4 <= kWaves * kPage * VSTR * 2, "merge slots must fit the V staging area");
-  static_assert(sizeof(FusedScratch) <= sizeof(vtile), "merge scratch must fit the V staging area");
+  static_assert(sizeof(FusedScratch<kThreads>) <= sizeof(vtile), "merge scratch must fit the V staging area");
 
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -712,84 +643,95 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
       } else {
         const int64_t ps = th * a.splits + split;
         float *po = a.part_o + ps * HD;
-        if (fused) {
 #pragma unroll
-          for (int jj = 0; jj < DJ; ++jj) store_coherent(po + 16 * jj + ln, oacc[jj][i]);
-          if (ln == 0) {
-            store_coherent(a.part_ml + 2 * ps, mo[i]);
-            store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
-          }
-        } else {
-#pragma unroll
-          for (int jj = 0; jj < DJ; ++jj) po[16 * jj + ln] = oacc[jj][i];
-          if (ln == 0) {
-            a.part_ml[2 * ps] = mo[i];
-            a.part_ml[2 * ps + 1] = lacc[i];
-          }
+        for (int jj = 0; jj < DJ; ++jj) store_coherent(po + 16 * jj + ln, oacc[jj][i]);
+        if (ln == 0) {
+          store_coherent(a.part_ml + 2 * ps, mo[i]);
+          store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
         }
       }
     }
   }
   if (!fused) return;
 
-  fused_merge<HD>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch *>(&vtile[0][0]), &s_is_last);
+  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]), &s_is_last);
 }
 
 // ---------------------------------------------------------------------------
 // Shared-page kernel: tiles of up to 64 columns (e.g. 8 rows x 8 heads of one
-// sequence) and every hd-512 tile.  The 4 waves stage each page's K and V in
-// LDS together with direct-to-LDS loads (global_load_lds_dwordx4) into a ring
-// of page buffers, NBUF-1 pages ahead of the page being computed.
+// sequence) and every hd-512 tile.  8 waves in two teams of 4; team t takes
+// the split's pages 2j + t, so every SIMD holds two waves whose latency chains
+// (LDS reads, MFMA, exp) overlap.  Both teams stage their pages' K and V in
+// LDS with direct-to-LDS loads (global_load_lds_dwordx4) into a ring of NP
+// slots of one page pair each, NP - 1 pairs ahead of the pair being computed.
 //   LDS K layout: MFMA operand order -- 16-byte chunk s is the A operand of
 //     step s / 64 for lane s % 64 (token s % 16, hd (4 (s/64) + (s/16) % 4) * 8).
 //   LDS V layout: [hd block of 16][token][16] -- the 16 lanes of a transpose
 //     read group cover 4 tokens x 16 columns contiguously.
-// The waves form 4/NSL column blocks x NSL hd slices: wave w scores column
-// block w / NSL over hd slice w % NSL; with NSL > 1 the slices' partial scores
-// are summed through LDS in slice order, so the waves of a block hold
-// identical scores and softmax state, and each accumulates P V for its own
-// slice.  NSL is fixed per launch (from the widest tile the shapes allow), so
-// every MFMA is unconditional.
-// Every wave waits for its own loads of a page, then a barrier makes the page
-// complete; the same barrier tells that the buffer refilled next is free.
+// Within a team the waves form 4/NSL column blocks x NSL hd slices: wave w
+// scores column block w / NSL over hd slice w % NSL; with NSL > 1 the slices'
+// partial scores are summed through LDS in slice order, so the waves of a
+// block hold identical scores and softmax state, and each accumulates P V for
+// its own slice.  NSL is fixed per launch (from the widest tile the shapes
+// allow), so every MFMA is unconditional.  At the end team 1's softmax state
+// is merged into team 0's in a fixed order.
+// Every wave waits for its own loads of a pair, then a barrier makes the pair
+// complete; the same barrier tells that the slot refilled next is free.
 // ---------------------------------------------------------------------------
+constexpr int kSharedThreads = 512;
 template <int HD, int NSL>
-__global__ __launch_bounds__(kThreads) void pgqa_shared_kernel(DecodeArgs a) {
+__global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;              // QK^T MFMA steps over the whole hd
   constexpr int DJ = HD / 16;              // PV MFMA output blocks over the whole hd
   constexpr int KS = KJ / NSL;             // ... per slice
   constexpr int DS = DJ / NSL;
-  constexpr int QBM = kWaves / NSL;        // column blocks per workgroup
+  constexpr int QBM = kWaves / NSL;        // column blocks per team
   constexpr int CAP = 16 * QBM;            // columns per tile
-  // LDS page buffers (separate objects, see below): four, three at hd 512
-  // (32 KB pages).
-  constexpr int NBUF = HD == 512 ? 3 : 4;
   constexpr int PAGE_ELEMS = kPage * HD;   // bf16 elements of one K (or V) page
+  constexpr int SLOT_ELEMS = 4 * PAGE_ELEMS;  // a page pair: team 0's K, V, then team 1's
+  constexpr int NP = HD == 512 ? 2 : HD == 256 ? 4 : 6;  // ring slots (128, 128, 96 KB)
   constexpr int LW = HD / 128;             // 1 KB direct loads per wave per page, each of K and V
-  constexpr int INFLIGHT = (NBUF - 2) * 2 * LW;  // this wave's loads still allowed in flight
+  constexpr int INFLIGHT = (NP - 2) * 2 * LW;  // this wave's loads still allowed in flight
+  constexpr int MCH = HD / 32 < DS ? HD / 32 : DS;  // output blocks per team-merge round
   static_assert(LW >= 1 && KS >= 1, "the shared-page kernel needs hd >= 128 and hd / 32 >= slices");
-  // One object per ring buffer and a page loop unrolled by NBUF, so every LDS
-  // access names its buffer at compile time and the compiler can tell reads
-  // of one buffer from the direct loads still landing in the others.
-  __shared__ __attribute__((aligned(16))) uint16_t stage0[2 * PAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t stage1[2 * PAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t stage2[2 * PAGE_ELEMS];
-  __shared__ __attribute__((aligned(16))) uint16_t stage3[NBUF > 3 ? 2 * PAGE_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) f32x4 xscore[kWaves][64];  // partial scores per wave
-  __shared__ float xfer[kWaves][16];
+  static_assert(DS % MCH == 0, "team merge rounds must cover the slice");
+  // One object per ring slot and a pair loop unrolled by NP, so every LDS
+  // access names its slot at compile time and the compiler can tell reads of
+  // one slot from the direct loads still landing in the others.
+  __shared__ __attribute__((aligned(16))) uint16_t slot0[SLOT_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t slot1[SLOT_ELEMS];
+  __shared__ __attribute__((aligned(16))) uint16_t slot2[NP > 2 ? SLOT_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot3[NP > 3 ? SLOT_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot4[NP > 4 ? SLOT_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) uint16_t slot5[NP > 5 ? SLOT_ELEMS : 8];
+  __shared__ __attribute__((aligned(16))) f32x4 xscore[2 * kWaves][64];  // partial scores per wave
+  __shared__ float xfer[2 * kWaves][16];
   __shared__ int s_is_last;
-  static_assert(sizeof(FusedScratch) <= sizeof(stage0), "merge scratch must fit a staging buffer");
-  uint16_t *const stage_ptr[4] = {stage0, stage1, stage2, stage3};
+  static_assert(sizeof(FusedScratch<kSharedThreads>) <= sizeof(slot0), "merge scratch must fit a ring slot");
+  static_assert(256 * MCH * 16 <= sizeof(slot0), "team merge round must fit a ring slot");
+  // Ring slot I as a direct reference to its own object (no pointer table):
+  // the compiler then knows which object every LDS access touches.
+  auto slot = [&](auto I) __attribute__((always_inline)) -> uint16_t * {
+    constexpr int i = decltype(I)::value;
+    if constexpr (i == 0) return slot0;
+    else if constexpr (i == 1) return slot1;
+    else if constexpr (i == 2) return slot2;
+    else if constexpr (i == 3) return slot3;
+    else if constexpr (i == 4) return slot4;
+    else return slot5;
+  };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int team = wave >> 2;  // wave-uniform
+  const int w4 = wave & 3;     // wave within the team
   const int ln = lane & 15;
   const int lc = lane >> 4;
-  const int cb = wave / NSL;  // this wave's column block
-  const int sl = wave % NSL;  // ... and hd slice
-  const int j0 = sl * KS;     // first QK step of the slice
-  const int jj0 = sl * DS;    // first PV block of the slice
+  const int cb = w4 / NSL;     // this wave's column block
+  const int sl = w4 % NSL;     // ... and hd slice
+  const int j0 = sl * KS;      // first QK step of the slice
+  const int jj0 = sl * DS;     // first PV block of the slice
 
   int b = blockIdx.x;
   const int split = b % a.splits;
@@ -797,264 +739,379 @@ __global__ __launch_bounds__(kThreads) void pgqa_shared_kernel(DecodeArgs a) {
   const int hb = b % a.hblocks;
   b /= a.hblocks;
   const int kh = b % a.nkv;
-  const int t0 = b / a.nkv;
+  // this workgroup's rmax-aligned block of rows; it takes the block's tiles
+  // (runs of rows on one sequence) one after another
+  const int rb0 = (b / a.nkv) * a.rmax;
+  const int rb1 = min(rb0 + a.rmax, a.rows);
+  for (int t0 = rb0; t0 < rb1;) {
+    const Tile tile = tile_rows(a, t0, lane);
+    const int nrows = tile.nrows;
+    int pbeg, pend;
+    split_range(tile, split, a.splits, pbeg, pend);
+    const int ncols = a.group <= CAP ? nrows * a.group : min(CAP, a.group - hb * CAP);
+    const bool active = 16 * cb < ncols;  // this wave's column block exists (wave-uniform)
 
-  const Tile tile = tile_rows(a, t0, lane);
-  if (!tile.lead) return;
-  const int nrows = tile.nrows;
-  int pbeg, pend;
-  split_range(tile, split, a.splits, pbeg, pend);
-  const int ncols = a.group <= CAP ? nrows * a.group : min(CAP, a.group - hb * CAP);
-  const bool active = 16 * cb < ncols;  // this wave's column block exists (wave-uniform)
-
-  const Column col = tile_column(16 * cb + ln, a.group, nrows, hb, CAP);
-  const int col_lo = __shfl(tile.lo_l, col.row);
-  // shuffle with every lane active, then drop columns without a row
-  const int col_hi_any = __shfl(tile.hi_l, col.row);
-  const int col_hi = col.on ? col_hi_any : -1;
-  bf16x8 qop[KS];
-  {
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (col.on ? col.row : 0)) * a.nh + kh * a.group + col.head) * HD;
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qop[u] = __builtin_bit_cast(bf16x8, z);
-      if (col.on) qop[u] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * (j0 + u) + lc) * 8);
-    }
-  }
-
-  float m_run = -INFINITY;
-  f32x4 oacc[DS];
-  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-  for (int u = 0; u < DS; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
-  const s16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
-  const int64_t kv_head_off = static_cast<int64_t>(kh) * kPage * HD;
-  const int64_t page_elems = static_cast<int64_t>(a.nkv) * kPage * HD;
-
-  // Global source (element offset in the page) of this lane's chunk of each
-  // of the wave's 1 KB direct loads: K chunk s = 64 i + lane, V chunk likewise.
-  int k_src[LW], v_src[LW];
-#pragma unroll
-  for (int r = 0; r < LW; ++r) {
-    const int s = (wave * LW + r) * 64 + lane;
-    k_src[r] = (s & 15) * HD + (4 * (s >> 6) + ((s >> 4) & 3)) * 8;
-    v_src[r] = ((s & 31) >> 1) * HD + (s >> 5) * 16 + (s & 1) * 8;
-  }
-
-  const int nk = pend - pbeg;
-  int pv0 = 0, pv1 = 0, pw0 = -1;  // physical pages of pages [pw0, pw0 + 128)
-  auto fetch_window = [&](int w0) {
-    int ph[2];
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-      const int k = w0 + 64 * h + lane;
-      ph[h] = 0;
-      if (k < nk) {
-        ph[h] = a.block_table[tile.origin + pbeg + k];
-        if (a.page_map) ph[h] = a.page_map[ph[h]];
+    const Column col = tile_column(16 * cb + ln, a.group, nrows, hb, CAP);
+    const int col_lo = __shfl(tile.lo_l, col.row);
+    // shuffle with every lane active, then drop columns without a row
+    const int col_hi_any = __shfl(tile.hi_l, col.row);
+    const int col_hi = col.on ? col_hi_any : -1;
+    bf16x8 qop[KS];
+    {
+      const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (col.on ? col.row : 0)) * a.nh + kh * a.group + col.head) * HD;
+  #pragma unroll
+      for (int u = 0; u < KS; ++u) {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[u] = __builtin_bit_cast(bf16x8, z);
+        if (col.on) qop[u] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * (j0 + u) + lc) * 8);
       }
     }
-    pv0 = ph[0];
-    pv1 = ph[1];
-    pw0 = w0;
-    wait_all_memory();
-  };
-  // Requests page k (clamped to the last page) into ring buffer dst.
-  auto issue_page = [&](int k, uint16_t *dst) {
-    k = min(k, nk - 1);
-    if (k - pw0 >= 128) fetch_window(k);  // drains the ring once per 128 pages
-    const int kw = k - pw0;
-    const int phys = kw < 64 ? __builtin_amdgcn_readlane(pv0, kw) : __builtin_amdgcn_readlane(pv1, kw - 64);
-    const int64_t page_off = static_cast<int64_t>(phys) * page_elems + kv_head_off;
-    const uint16_t *kp = a.k_pool + page_off;
-    const uint16_t *vp = a.v_pool + page_off;
-    uint16_t *kdst = dst + wave * LW * 512;
-    uint16_t *vdst = dst + PAGE_ELEMS + wave * LW * 512;
-#pragma unroll
+
+    float m_run = -INFINITY;  // reference max (log2 units) of column ln, the same in the column's 4 lanes
+    f32x4 oacc[DS];
+    f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+    for (int u = 0; u < DS; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const s16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
+    const int64_t kv_head_off = static_cast<int64_t>(kh) * kPage * HD;
+    const int64_t page_elems = static_cast<int64_t>(a.nkv) * kPage * HD;
+
+    // Global source (element offset in the page) of this lane's chunk of each
+    // of the wave's 1 KB direct loads: K chunk s = 64 i + lane, V chunk likewise.
+    int k_src[LW], v_src[LW];
+  #pragma unroll
     for (int r = 0; r < LW; ++r) {
-      load_to_lds16(kp + k_src[r], kdst + r * 512);
-      load_to_lds16(vp + v_src[r], vdst + r * 512);
+      const int s = (w4 * LW + r) * 64 + lane;
+      k_src[r] = (s & 15) * HD + (4 * (s >> 6) + ((s >> 4) & 3)) * 8;
+      v_src[r] = ((s & 31) >> 1) * HD + (s >> 5) * 16 + (s & 1) * 8;
     }
-  };
 
-  // One page: wait for it, refill the buffer of the page before it, compute it.
-  auto step = [&](int k, const uint16_t *kt, uint16_t *refill) {
-    // this wave's loads of page k have landed once at most the newer pages'
-    // loads are outstanding; the barrier then makes the whole page visible and
-    // tells that the buffer of page k - 1 is no longer read
-    __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0f70);
-    lds_barrier();
-    issue_page(k + NBUF - 1, refill);
-    if (k >= nk) return;
-
-    const int p = pbeg + k;
-    const bool full = p >= tile.fp0 && p < tile.fp1;  // the same in every wave
-    uint32_t tokmask = 0xffffu;
-    if (!full) {
-      // tokens of this page some row of the tile can see
-      uint32_t mrow = 0;
-      if (lane < nrows) {
-        const int lo = max(tile.lo_l - p * kPage, 0), hi = min(tile.hi_l - p * kPage, kPage - 1);
-        if (hi >= lo) mrow = ((2u << hi) - 1u) & ~((1u << lo) - 1u);
-      }
-#pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) mrow |= __shfl_xor(mrow, off);
-      tokmask = __builtin_amdgcn_readfirstlane(mrow);
-    }
-    if (tokmask == 0) return;  // the same in every wave
-
-    const uint16_t *vt = kt + PAGE_ELEMS;
-    // partial scores over this wave's hd slice: all K operands read first,
-    // two accumulation chains
-    bf16x8 kop[KS];
-#pragma unroll
-    for (int u = 0; u < KS; ++u) kop[u] = *reinterpret_cast<const bf16x8 *>(kt + ((j0 + u) * 64 + lane) * 8);
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f}, sc1 = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int u = 0; u < KS; ++u) {
-      if ((u & 1) == 0) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc, 0, 0, 0);
-      else sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc1, 0, 0, 0);
-    }
-    if constexpr (KS > 1) sc += sc1;
-    if constexpr (NSL > 1) {
-      xscore[wave][lane] = sc;
-      lds_barrier();
-      sc = xscore[cb * NSL][lane];
-#pragma unroll
-      for (int s2 = 1; s2 < NSL; ++s2) sc += xscore[cb * NSL + s2][lane];
-    }
-    if (!active) return;
-
-    bool vis[4] = {true, true, true, true};
-    if (!full) {
-      const int pos0 = p * kPage + 4 * lc;
-#pragma unroll
-      for (int t = 0; t < 4; ++t) vis[t] = pos0 + t >= col_lo && pos0 + t <= col_hi;
-    }
-    float sv[4];
-    float mx = -INFINITY;
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      sv[t] = vis[t] ? sc[t] : -INFINITY;
-      mx = fmaxf(mx, sv[t]);
-    }
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m2 = mx * kLog2e;
-    const bool grow = m2 > m_run + kRescaleSlack;
-    if (__ballot(grow) != 0) {
-      const float m_new = grow ? m2 : m_run;
-      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
-      m_run = m_new;
-      if (lc == 0) xfer[wave][ln] = alpha;
-      wave_lds_sync();
-      const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
-#pragma unroll
-      for (int u = 0; u < DS; ++u) oacc[u] *= al;
-      lacc *= al;
-    }
-    float pr[4];
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      pr[t] = fast_exp2(__builtin_fmaf(sv[t], kLog2e, -m_run));
-      if (!full) pr[t] = sv[t] == -INFINITY ? 0.f : pr[t];
-    }
-    const s16x4 pa = pack_weights(pr[0], pr[1], pr[2], pr[3]);
-    // lane (4m+q) of group lc reads token 4 lc + m, columns 4q..4q+3 of each block
-    const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * 16 + 4 * (ln & 3) + jj0 * 256;
-    // tokens no column can see may hold NaN: zero their V entries (slow path)
-    const uint32_t keep = (tokmask >> (4 * lc)) & 0xfu;
-    s16x4 vb[DS];
-#pragma unroll
-    for (int u = 0; u < DS; ++u)
-      vb[u] = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4 *)(vtr + u * 256));
-#pragma unroll
-    for (int u = 0; u < DS; ++u) {
-      if (!full) {
-#pragma unroll
-        for (int r = 0; r < 4; ++r) vb[u][r] = (keep >> r) & 1u ? vb[u][r] : static_cast<short>(0);
-      }
-      oacc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[u], oacc[u], 0, 0, 0);
-    }
-    lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
-  };
-
-  if (nk > 0) {
-    fetch_window(0);
-#pragma unroll
-    for (int i = 0; i < NBUF - 1; ++i) issue_page(i, stage_ptr[i]);
-    if constexpr (NBUF == 4) {
-      for (int k = 0; k < nk; k += 4) {
-        step(k, stage_ptr[0], stage_ptr[3]);
-        step(k + 1, stage_ptr[1], stage_ptr[0]);
-        step(k + 2, stage_ptr[2], stage_ptr[1]);
-        step(k + 3, stage_ptr[3], stage_ptr[2]);
-      }
-    } else {
-      for (int k = 0; k < nk; k += 3) {
-        step(k, stage_ptr[0], stage_ptr[2]);
-        step(k + 1, stage_ptr[1], stage_ptr[0]);
-        step(k + 2, stage_ptr[2], stage_ptr[1]);
-      }
-    }
-  }
-  wait_all_memory();  // the ring's trailing (repeated) loads have landed
-  __syncthreads();
-
-  // ---- results: this wave's hd slice of its column block ----
-  const bool fused = a.splits > 1 && a.counters != nullptr;
-  if (active) {
-    if (lc == 0) xfer[wave][ln] = m_run;
-    wave_lds_sync();
-    const f32x4 mo = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = 16 * cb + 4 * lc + i;
-      if (r >= ncols) continue;
-      const Column rc = tile_column(r, a.group, nrows, hb, CAP);
-      const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      if (a.splits == 1) {
-        const float l = lacc[i];
-#pragma unroll
-        for (int u = 0; u < DS; ++u) {
-          const float v = l > 0.f ? oacc[u][i] / l : 0.f;
-          a.out[th * HD + 16 * (jj0 + u) + ln] = f32_to_bf16_rne(v);
+    const int nk = pend - pbeg;
+    const int npairs = (nk + 1) / 2;
+    int pv0 = 0, pv1 = 0, pw0 = -1;  // physical pages of pages [pw0, pw0 + 128)
+    auto fetch_window = [&](int w0) __attribute__((always_inline)) {
+      int ph[2];
+  #pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        const int k = w0 + 64 * h + lane;
+        ph[h] = 0;
+        if (k < nk) {
+          ph[h] = a.block_table[tile.origin + pbeg + k];
+          if (a.page_map) ph[h] = a.page_map[ph[h]];
         }
-      } else {
-        const int64_t ps = th * a.splits + split;
-        float *po = a.part_o + ps * HD + 16 * jj0;
-        if (fused) {
-#pragma unroll
+      }
+      pv0 = ph[0];
+      pv1 = ph[1];
+      pw0 = w0;
+      wait_all_memory();
+    };
+    // Requests this team's page of pair j into ring slot `dst`.  Past the
+    // split's end it requests the last page again: every step issues the same
+    // number of loads, so the counted waits below stay exact (and the compiler
+    // can tell which loads an LDS read must wait for).
+    auto issue_pair = [&](int j, uint16_t *dst) __attribute__((always_inline)) {
+      const int k = min(2 * j + team, nk - 1);
+      if (k - pw0 >= 128) fetch_window(k - team);  // drains the ring once per 128 pages
+      const int kw = k - pw0;
+      const int phys = kw < 64 ? __builtin_amdgcn_readlane(pv0, kw) : __builtin_amdgcn_readlane(pv1, kw - 64);
+      const int64_t page_off = static_cast<int64_t>(phys) * page_elems + kv_head_off;
+      const uint16_t *kp = a.k_pool + page_off;
+      const uint16_t *vp = a.v_pool + page_off;
+      uint16_t *kdst = dst + team * 2 * PAGE_ELEMS + w4 * LW * 512;
+      uint16_t *vdst = kdst + PAGE_ELEMS;
+  #pragma unroll
+      for (int r = 0; r < LW; ++r) {
+        load_to_lds16(kp + k_src[r], kdst + r * 512);
+        load_to_lds16(vp + v_src[r], vdst + r * 512);
+      }
+    };
+
+    // One pair: wait for it, refill the slot of the pair before it, compute this
+    // team's page of it.
+    auto step = [&](int j, const uint16_t *buf, uint16_t *refill) __attribute__((always_inline)) {
+      // this wave's loads of pair j have landed once at most the loads of the
+      // pairs after it are outstanding; the barrier then makes the whole pair
+      // visible and tells that the slot of pair j - 1 is no longer read
+      __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0f70);
+      lds_barrier();
+      issue_pair(j + NP - 1, refill);
+
+      const int k = 2 * j + team;
+      const int p = pbeg + k;
+      const bool full = p >= tile.fp0 && p < tile.fp1;  // the same in every wave of the team
+      uint32_t tokmask = 0;
+      if (k < nk) {
+        tokmask = 0xffffu;
+        if (!full) {
+          // tokens of this page some row of the tile can see
+          uint32_t mrow = 0;
+          if (lane < nrows) {
+            const int lo = max(tile.lo_l - p * kPage, 0), hi = min(tile.hi_l - p * kPage, kPage - 1);
+            if (hi >= lo) mrow = ((2u << hi) - 1u) & ~((1u << lo) - 1u);
+          }
+  #pragma unroll
+          for (int off = 32; off >= 1; off >>= 1) mrow |= __shfl_xor(mrow, off);
+          tokmask = __builtin_amdgcn_readfirstlane(mrow);
+        }
+      }
+      const bool work = tokmask != 0;  // the same in every wave of the team
+
+      const uint16_t *kt = buf + team * 2 * PAGE_ELEMS;
+      const uint16_t *vt = kt + PAGE_ELEMS;
+      // lane (4m+q) of group lc reads token 4 lc + m, columns 4q..4q+3 of each block
+      const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * 16 + 4 * (ln & 3) + jj0 * 256;
+      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+      s16x4 vb[DS];
+      if (work) {
+        // partial scores over this wave's hd slice: all K operands read first,
+        // two accumulation chains; V operands requested meanwhile
+        bf16x8 kop[KS];
+  #pragma unroll
+        for (int u = 0; u < KS; ++u) kop[u] = *reinterpret_cast<const bf16x8 *>(kt + ((j0 + u) * 64 + lane) * 8);
+        {
+          const uint32_t va = lds_address(vtr);
+          [&]<int... U>(std::integer_sequence<int, U...>) {
+            ((vb[U] = lds_read_tr16<U * 512>(va)), ...);
+          }(std::make_integer_sequence<int, DS>{});
+        }
+        f32x4 sc1 = {0.f, 0.f, 0.f, 0.f};
+  #pragma unroll
+        for (int u = 0; u < KS; ++u) {
+          if ((u & 1) == 0) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc, 0, 0, 0);
+          else sc1 = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kop[u], qop[u], sc1, 0, 0, 0);
+        }
+        if constexpr (KS > 1) sc += sc1;
+      }
+      if constexpr (NSL > 1) {
+        // every wave of both teams takes part in the exchange barrier
+        if (work) xscore[wave][lane] = sc;
+        lds_barrier();
+        if (work) {
+          sc = xscore[4 * team + cb * NSL][lane];
+  #pragma unroll
+          for (int s2 = 1; s2 < NSL; ++s2) sc += xscore[4 * team + cb * NSL + s2][lane];
+        }
+      }
+      if (!work || !active) return;
+
+      bool vis[4] = {true, true, true, true};
+      if (!full) {
+        const int pos0 = p * kPage + 4 * lc;
+  #pragma unroll
+        for (int t = 0; t < 4; ++t) vis[t] = pos0 + t >= col_lo && pos0 + t <= col_hi;
+      }
+      float sv[4];
+      float lmx = -INFINITY;
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        sv[t] = vis[t] ? sc[t] : -INFINITY;
+        lmx = fmaxf(lmx, sv[t]);
+      }
+      // The column's reference max moves only when one of its scores passes it
+      // by more than the slack; only then is the column max taken across lanes.
+      if (__ballot(lmx * kLog2e > m_run + kRescaleSlack) != 0) {
+        float mx = lmx;
+        mx = fmaxf(mx, __shfl_xor(mx, 16));
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        const float m2 = mx * kLog2e;
+        const bool grow = m2 > m_run + kRescaleSlack;  // the same in the column's 4 lanes
+        const float m_new = grow ? m2 : m_run;
+        const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+        m_run = m_new;
+        if (lc == 0) xfer[wave][ln] = alpha;
+        wave_lds_sync();
+        const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+  #pragma unroll
+        for (int u = 0; u < DS; ++u) oacc[u] *= al;
+        lacc *= al;
+      }
+      float pr[4];
+  #pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        pr[t] = fast_exp2(__builtin_fmaf(sv[t], kLog2e, -m_run));
+        if (!full) pr[t] = sv[t] == -INFINITY ? 0.f : pr[t];
+      }
+      const s16x4 pa = pack_weights(pr[0], pr[1], pr[2], pr[3]);
+      lds_wait_reads();  // the V operands have arrived
+      if (!full) {
+        // tokens no column can see may hold NaN: zero their V entries
+        const uint32_t keep = (tokmask >> (4 * lc)) & 0xfu;
+  #pragma unroll
+        for (int u = 0; u < DS; ++u)
+  #pragma unroll
+          for (int r = 0; r < 4; ++r) vb[u][r] = (keep >> r) & 1u ? vb[u][r] : static_cast<short>(0);
+      }
+  #pragma unroll
+      for (int u = 0; u < DS; ++u) oacc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb[u], oacc[u], 0, 0, 0);
+      lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
+    };
+
+    if (npairs > 0) {
+      fetch_window(0);
+      [&]<int... I>(std::integer_sequence<int, I...>) {
+        (issue_pair(I, slot(std::integral_constant<int, I>{})), ...);
+      }(std::make_integer_sequence<int, NP - 1>{});
+      for (int j = 0; j < npairs; j += NP) {
+        [&]<int... I>(std::integer_sequence<int, I...>) {
+          (step(j + I, slot(std::integral_constant<int, I>{}), slot(std::integral_constant<int, (I + NP - 1) % NP>{})), ...);
+        }(std::make_integer_sequence<int, NP>{});
+      }
+    }
+    wait_all_memory();
+    __syncthreads();
+
+    // ---- team 1's state joins team 0's: per column, the larger reference max
+    // wins and both sums are scaled to it (team 0 first) ----
+    float mo[4], lo[4];
+    {
+      if (lc == 0) xfer[wave][ln] = m_run;
+      wave_lds_sync();
+      const f32x4 m4 = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        mo[i] = m4[i];
+        lo[i] = lacc[i];
+      }
+    }
+    float sa[4] = {1.f, 1.f, 1.f, 1.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
+    f32x4 *xm = reinterpret_cast<f32x4 *>(&xscore[0][0]);  // [w4][lane] (m x4, l x4)
+    __syncthreads();
+    if (team == 1) {
+      xm[(w4 * 64 + lane) * 2] = f32x4{mo[0], mo[1], mo[2], mo[3]};
+      xm[(w4 * 64 + lane) * 2 + 1] = f32x4{lo[0], lo[1], lo[2], lo[3]};
+    }
+    __syncthreads();
+    if (team == 0) {
+      const f32x4 mb = xm[(w4 * 64 + lane) * 2];
+      const f32x4 lb = xm[(w4 * 64 + lane) * 2 + 1];
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float mm = fmaxf(mo[i], mb[i]);
+        sa[i] = mm == -INFINITY ? 0.f : fast_exp2(mo[i] - mm);
+        sb[i] = mm == -INFINITY ? 0.f : fast_exp2(mb[i] - mm);
+        lo[i] = lo[i] * sa[i] + lb[i] * sb[i];
+        mo[i] = mm;
+      }
+    }
+    {
+      f32x4 *xo = reinterpret_cast<f32x4 *>(slot0);  // [w4][u][lane]
+  #pragma unroll
+      for (int u0 = 0; u0 < DS; u0 += MCH) {
+        __syncthreads();
+        if (team == 1) {
+  #pragma unroll
+          for (int u = 0; u < MCH; ++u) xo[(w4 * MCH + u) * 64 + lane] = oacc[u0 + u];
+        }
+        __syncthreads();
+        if (team == 0) {
+  #pragma unroll
+          for (int u = 0; u < MCH; ++u) {
+            const f32x4 ob = xo[(w4 * MCH + u) * 64 + lane];
+  #pragma unroll
+            for (int i = 0; i < 4; ++i) oacc[u0 + u][i] = oacc[u0 + u][i] * sa[i] + ob[i] * sb[i];
+          }
+        }
+      }
+    }
+
+    // ---- results: team 0, this wave's hd slice of its column block ----
+    const bool fused = a.splits > 1 && a.counters != nullptr;
+    if (team == 0 && active) {
+  #pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int r = 16 * cb + 4 * lc + i;
+        if (r >= ncols) continue;
+        const Column rc = tile_column(r, a.group, nrows, hb, CAP);
+        const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+        if (a.splits == 1) {
+          const float l = lo[i];
+  #pragma unroll
+          for (int u = 0; u < DS; ++u) {
+            const float v = l > 0.f ? oacc[u][i] / l : 0.f;
+            a.out[th * HD + 16 * (jj0 + u) + ln] = f32_to_bf16_rne(v);
+          }
+        } else {
+          const int64_t ps = th * a.splits + split;
+          float *po = a.part_o + ps * HD + 16 * jj0;
+  #pragma unroll
           for (int u = 0; u < DS; ++u) store_coherent(po + 16 * u + ln, oacc[u][i]);
           if (sl == 0 && ln == 0) {
             store_coherent(a.part_ml + 2 * ps, mo[i]);
-            store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
-          }
-        } else {
-#pragma unroll
-          for (int u = 0; u < DS; ++u) po[16 * u + ln] = oacc[u][i];
-          if (sl == 0 && ln == 0) {
-            a.part_ml[2 * ps] = mo[i];
-            a.part_ml[2 * ps + 1] = lacc[i];
+            store_coherent(a.part_ml + 2 * ps + 1, lo[i]);
           }
         }
       }
     }
+    __syncthreads();  // the team-merge area (slot 0) is free again
+    if (fused)
+      fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
+                                      reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
+    t0 += nrows;
+    __syncthreads();  // LDS is reused by the next tile
   }
-  if (!fused) return;
-  fused_merge<HD>(a, t0, kh, hb, nrows, ncols, CAP, reinterpret_cast<FusedScratch *>(stage_ptr[0]), &s_is_last);
 }
 
-// Separate merge: one workgroup per (row, query head, chunk of hd).
-template <int NB>
+// Separate merge: one workgroup per (row, query head, 32 hd elements).
+// Thread (g, e) = (tid / 32, tid % 32) owns element e of the chunk for the
+// splits s = g mod 8.  Every load -- the (m, l) of all splits and the thread's
+// partial elements -- is issued before any is used, so the merge costs one
+// memory round trip.
+constexpr int kCombineSplits = kMaxSplits / kMergeGroups;  // splits per thread
 __global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, int hd) {
-  __shared__ MergeScratch ms;
-  const int chunks = hd / (32 * NB);
+  __shared__ float w_s[kMaxSplits], l_s[kMaxSplits], red[kWaves], dgrp[kMergeGroups];
+  __shared__ float acc[kMergeGroups][32];
+  const int tid = threadIdx.x;
+  const int g = tid >> 5, e = tid & 31;
+  const int chunks = hd / 32;
   const int64_t th = blockIdx.x / chunks;
-  const int d0 = (blockIdx.x - th * chunks) * 32 * NB;
-  const float den = merge_weights(LoadPlain{}, a.part_ml + th * a.splits * 2, a.splits, ms);
-  merge_chunk<NB>(LoadPlain{}, a.part_o + th * a.splits * hd, a.splits, hd, d0, den, ms, a.out + th * hd);
+  const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
+  const int S = a.splits;
+  const float *ml = a.part_ml + th * S * 2;
+  const float *o = a.part_o + th * S * hd + d0 + e;
+  const int sm = min(tid, S - 1);
+  const float m = ml[2 * sm], l = ml[2 * sm + 1];
+  float v[kCombineSplits];
+#pragma unroll
+  for (int i = 0; i < kCombineSplits; ++i) v[i] = o[static_cast<int64_t>(min(g + kMergeGroups * i, S - 1)) * hd];
+
+  const bool live = tid < S && l > 0.f;
+  float mx = live ? m : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
+  w_s[tid] = live ? fast_exp2(m - mx) : 0.f;
+  l_s[tid] = l;
+  __syncthreads();
+  if (tid < kMergeGroups) {
+    float dg = 0.f;
+    for (int s = tid; s < S; s += kMergeGroups) {
+      const float ws = w_s[s];
+      dg = ws != 0.f ? __builtin_fmaf(ws, l_s[s], dg) : dg;
+    }
+    dgrp[tid] = dg;
+  }
+  float num = 0.f;
+#pragma unroll
+  for (int i = 0; i < kCombineSplits; ++i) {
+    const int s = g + kMergeGroups * i;
+    if (s < S) {
+      const float ws = w_s[s];
+      num = ws != 0.f ? __builtin_fmaf(ws, v[i], num) : num;
+    }
+  }
+  acc[g][e] = num;
+  __syncthreads();
+  if (tid < 32) {
+    float n = 0.f, den = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < kMergeGroups; ++gg) {
+      n += acc[gg][tid];
+      den += dgrp[gg];
+    }
+    a.out[th * hd + d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
+  }
 }
 
 thread_local char g_error[512] = "";
@@ -1090,6 +1147,7 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
   p.kind = hd == 512 || (hd >= 128 && cols > 16 && group >= 8) ? 1 : 0;
   p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
   if (p.kind == 1 && hd == 128 && p.nsl == 4) p.nsl = 2;  // hd 128 has 4 QK steps
+  if (p.kind == 1 && hd == 512 && p.nsl == 1) p.nsl = 2;  // a whole hd-512 slice needs too many registers
   p.cap = p.kind == 1 ? 16 * (kWaves / p.nsl) : 16;
   p.rmax = group <= p.cap ? static_cast<int>(p.cap / group) : 1;
   p.hblocks = group <= p.cap ? 1 : static_cast<int>((group + p.cap - 1) / p.cap);
@@ -1101,10 +1159,24 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if constexpr (HD >= 128) {
     if (p.kind == 1) {
-      if (p.nsl == 1) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 1>), grid, block, 0, stream, a);
-      else if (p.nsl == 2) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 2>), grid, block, 0, stream, a);
-      else if constexpr (HD >= 256) hipLaunchKernelGGL((pgqa_shared_kernel<HD, 4>), grid, block, 0, stream, a);
-      return hipGetLastError();
+      const dim3 sblock(kSharedThreads);
+      if (p.nsl == 2) {
+        hipLaunchKernelGGL((pgqa_shared_kernel<HD, 2>), grid, sblock, 0, stream, a);
+        return hipGetLastError();
+      }
+      if constexpr (HD < 512) {
+        if (p.nsl == 1) {
+          hipLaunchKernelGGL((pgqa_shared_kernel<HD, 1>), grid, sblock, 0, stream, a);
+          return hipGetLastError();
+        }
+      }
+      if constexpr (HD >= 256) {
+        if (p.nsl == 4) {
+          hipLaunchKernelGGL((pgqa_shared_kernel<HD, 4>), grid, sblock, 0, stream, a);
+          return hipGetLastError();
+        }
+      }
+      return hipErrorInvalidValue;
     }
   }
   if constexpr (HD < 512) {
@@ -1171,13 +1243,15 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
 
   const int64_t group = nh / nkv;
   const Plan plan = make_plan(rows, group, hd);
-  const int64_t units = rows * nkv * plan.hblocks;
+  // the per-wave kernel's workgroups each take one row (working only if it
+  // starts a tile); the shared-page kernel's an rmax-aligned block of rows
+  const int64_t grid_rows = plan.kind == 1 ? (rows + plan.rmax - 1) / plan.rmax : rows;
   // the documented (kernel-independent) bound: at most rows * nkv * ceil(group / 16) units
   if (counters && splits > 1 && rows * nkv * ((group + 15) / 16) > kCounterCap)
     return fail(PGQA_ECAP, "rows * nkv * ceil(group / 16) = %lld exceeds the %d counters",
                 (long long)(rows * nkv * ((group + 15) / 16)), kCounterCap);
   if (rows * nh * (hd > 128 ? hd / 128 : 1) > INT_MAX) return fail(PGQA_EINVAL, "rows * nh too large");
-  const int64_t blocks = units * splits;
+  const int64_t blocks = grid_rows * nkv * plan.hblocks * splits;
   if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
 
   DecodeArgs a;
@@ -1213,12 +1287,8 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {
-    if (hd == 64)
-      hipLaunchKernelGGL(pgqa_combine_kernel<2>, dim3(static_cast<unsigned>(rows * nh)), dim3(kThreads), 0, st, a,
-                         static_cast<int>(hd));
-    else
-      hipLaunchKernelGGL(pgqa_combine_kernel<4>, dim3(static_cast<unsigned>(rows * nh * (hd / 128))), dim3(kThreads), 0,
-                         st, a, static_cast<int>(hd));
+    hipLaunchKernelGGL(pgqa_combine_kernel, dim3(static_cast<unsigned>(rows * nh * (hd / 32))), dim3(kThreads), 0, st,
+                       a, static_cast<int>(hd));
     err = hipGetLastError();
     if (err != hipSuccess) return fail(PGQA_ELAUNCH, "combine kernel launch: %s", hipGetErrorString(err));
   }
