@@ -237,6 +237,58 @@ __device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane)
   return t;
 }
 
+// The row of rank p when the rows are ordered by decreasing visible length
+// (ties: lower row first), the same in every lane.  Workgroups take rows in
+// this order, so the first dispatched take the longest rows and a batch of
+// uneven sequences ends on short pieces of work, not on one long row.  Rank
+// selection is a binary search on the length with wave-wide counts.  Batches
+// of more than kRankRows rows keep their own order.
+constexpr int kRankRows = 1024;
+constexpr int kRankLenMax = (1 << 30) - 1;  // longer rows rank as equals
+__device__ __forceinline__ int row_of_rank(const DecodeArgs &a, int p, int lane) {
+  if (a.rows > kRankRows) return p;
+  constexpr int R = kRankRows / 64;
+  const int nr = (a.rows + 63) / 64;
+  int len[R];
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    const int r = 64 * k + lane;
+    len[k] = -1;
+    if (k < nr && r < a.rows) {
+      const int lo = a.window > 0 ? max(0, a.qpos[r] + 1 - a.window) : 0;
+      len[k] = min(max(a.kv_last[r] - lo + 1, 0), kRankLenMax);
+    }
+  }
+  auto count_gt = [&](int x) {
+    int c = 0;
+#pragma unroll
+    for (int k = 0; k < R; ++k)
+      if (k < nr) c += __builtin_popcountll(__ballot(len[k] > x));
+    return c;
+  };
+  // smallest length x with at most p rows longer than x: the rank-p length
+  int lo_x = -1, hi_x = kRankLenMax;
+  while (hi_x - lo_x > 1) {
+    const int mid = lo_x + (hi_x - lo_x) / 2;
+    if (count_gt(mid) <= p) hi_x = mid;
+    else lo_x = mid;
+  }
+  int q = p - count_gt(hi_x);  // position among the rows of that length
+#pragma unroll
+  for (int k = 0; k < R; ++k) {
+    if (k < nr) {
+      uint64_t m = __ballot(len[k] == hi_x);
+      const int c = __builtin_popcountll(m);
+      if (q < c) {
+        for (int i = 0; i < q; ++i) m &= m - 1;
+        return 64 * k + static_cast<int>(__builtin_ctzll(m));
+      }
+      q -= c;
+    }
+  }
+  return p;  // not reached
+}
+
 // Split `split` of S covers pages [pbeg, pend) of the tile's visible page
 // range [lo_min / 16, hi_max / 16], cut into S contiguous near-equal chunks
 // from logical positions only (some may be empty).
@@ -380,7 +432,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   const int hb = b % a.hblocks;
   b /= a.hblocks;
   const int kh = b % a.nkv;
-  const int t0 = b / a.nkv;
+  const int t0 = row_of_rank(a, b / a.nkv, lane);
 
   // ---- tile; Q for every possible column is requested in the same round ----
   const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
