@@ -73,6 +73,7 @@ struct DecodeArgs {
   const int32_t *page_map;
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
+  int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
 };
 
 // Orders this wave's LDS accesses around the point (a wave executes its LDS
@@ -241,12 +242,13 @@ __device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane)
 // (ties: lower row first), the same in every lane.  Workgroups take rows in
 // this order, so the first dispatched take the longest rows and a batch of
 // uneven sequences ends on short pieces of work, not on one long row.  Rank
-// selection is a binary search on the length with wave-wide counts.  Batches
-// of more than kRankRows rows keep their own order.
+// selection is a binary search on the length with wave-wide counts.  Small
+// launches and batches of more than kRankRows rows keep their own order.
 constexpr int kRankRows = 1024;
+constexpr int64_t kRankMinBlocks = 1024;  // launches this large take rows longest first
 constexpr int kRankLenMax = (1 << 30) - 1;  // longer rows rank as equals
 __device__ __forceinline__ int row_of_rank(const DecodeArgs &a, int p, int lane) {
-  if (a.rows > kRankRows) return p;
+  if (!a.rank_rows || a.rows > kRankRows) return p;
   constexpr int R = kRankRows / 64;
   const int nr = (a.rows + 63) / 64;
   int len[R];
@@ -1248,10 +1250,11 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
   const int64_t units = nseq * nkv;
   const int64_t pages = (kv_span + kPage - 1) / kPage;
-  // Aim at about 8 workgroups per CU on the 256 CUs (uneven sequence lengths
-  // then still balance), with at least 16 pages in a split of a long span and
-  // up to 8 splits of at least 4 pages for a short one.
-  const int64_t target = 2048;
+  // Aim at about 6 workgroups per CU on the 256 CUs (with the longest rows
+  // dispatched first, uneven sequence lengths then still balance), with at
+  // least 16 pages in a split of a long span and up to 8 splits of at least 4
+  // pages for a short one.
+  const int64_t target = 1536;
   int64_t s = (target + units - 1) / units;
   int64_t smax = pages / 4 < 8 ? pages / 4 : 8;
   if (pages / 16 > smax) smax = pages / 16;
@@ -1328,6 +1331,10 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   a.rmax = plan.rmax;
   a.hblocks = plan.hblocks;
   a.cap = plan.cap;
+  // Ordering rows costs a dependent memory round trip before a workgroup can
+  // start; it pays only when the launch is several times what the GPU holds
+  // at once, so that the order of dispatch decides how the launch ends.
+  a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
 
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;

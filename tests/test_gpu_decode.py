@@ -148,6 +148,16 @@ def edge_workloads():
     qp = (b.qpos[seq] - back).astype(np.int32)
     cases.append(b.replace(name="mixed", rows=len(seq), q=np.concatenate([b.q, b.q, b.q])[:len(seq)],
                            page_origin=b.page_origin[seq].copy(), qpos=qp, kv_last=qp.copy()))
+    # a large launch of multi-row tiles (16 sequences x 4 rows, MHA): with 5
+    # splits it is big enough for the per-wave kernel to take rows longest first
+    r = workloads.batched("ranked", nseq=16, lmin=20, lmax=3000, nh=8, nkv=8, hd=64, pad=16)
+    seq = np.repeat(np.arange(16), 4)
+    back = np.tile(np.arange(3, -1, -1), 16)
+    qp = (r.qpos[seq] - back).astype(np.int32)
+    rq = np.random.default_rng(3).standard_normal((len(seq), r.nh, r.hd)).astype(np.float32)
+    rq = (rq.view(np.uint32) >> 16).astype(np.uint16)
+    cases.append(r.replace(name="ranked", rows=len(seq), q=rq, page_origin=r.page_origin[seq].copy(),
+                           qpos=qp, kv_last=qp.copy()))
     # wide group (32 heads per kv head -> two head blocks), nkv=1
     cases.append(rng_seq("g32", ctx=333, rows=2, nh=32, nkv=1, hd=64, window=0))
     # plain MHA (group 1): 16 rows share each page
