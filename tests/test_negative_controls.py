@@ -1,0 +1,135 @@
+"""Negative controls: every gate the GPU path must pass has to turn red when a
+plausible mistake is planted.  The mistakes are planted on the CPU -- in the
+oracle's inputs or addressing, or in a plain model of the merge and its
+counter protocol -- never in the HIP path.
+
+Gates (span-02 GPU test page, engine/crates/kernels/tests/gpu.rs, `run()`):
+rel-RMS < 1e-2 against the f64 reference, fused merge == separate combine bit
+for bit, counters back to zero after a call.
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+TOL = 1e-2
+
+
+def red(ref, got):
+    """The rel-RMS gate fails (a NaN counts as failing)."""
+    e = oracle.rel_rms(got, ref)
+    return not (e < TOL)
+
+
+@pytest.fixture(scope="module")
+def pa():
+    w = workloads.make("PA")
+    return w, oracle.decode(w)
+
+
+def test_page_address_off_by_one_slot_is_caught(pa):
+    """Reading token slot p % 16 + 1 instead of p % 16."""
+    w, ref = pa
+    shifted = w.replace(k_pool=np.roll(w.k_pool, -1, axis=2), v_pool=np.roll(w.v_pool, -1, axis=2))
+    assert red(ref, oracle.decode(shifted))
+
+
+def test_page_address_off_by_one_page_is_caught(pa):
+    """Reading the block-table entry after the right one."""
+    w, ref = pa
+    bt = np.concatenate([w.block_table[1:], w.block_table[-1:]]).astype(np.int32)
+    assert red(ref, oracle.decode(w.replace(block_table=bt)))
+
+
+def test_origins_forced_to_zero_is_caught():
+    """Row origins ignored in a batch: rows read the pad entries (NaN page 0)
+    and other sequences' pages."""
+    w = workloads.batched("neg", nseq=6, lmin=40, lmax=400, nh=4, nkv=2, hd=64, pad=16)
+    ref = oracle.decode(w)
+    bad = oracle.decode(w.replace(page_origin=np.zeros_like(w.page_origin)))
+    assert red(ref, bad)
+
+
+def test_rows_pinned_to_row_zero_window_is_caught():
+    """Every row of a multi-row call using row 0's visible range."""
+    w = workloads.single_sequence("neg2", ctx=300, rows=6, nh=4, nkv=1, hd=64, window=7)
+    ref = oracle.decode(w)
+    pinned = w.replace(qpos=np.full_like(w.qpos, w.qpos[0]), kv_last=np.full_like(w.kv_last, w.kv_last[0]))
+    bad = oracle.decode(pinned)
+    # row 0 itself is unchanged; every other row moves
+    assert np.array_equal(bad[0], ref[0])
+    assert red(ref[1:], bad[1:])
+
+
+def test_window_off_by_one_is_caught():
+    """lo = qpos - window (one key too many) instead of qpos + 1 - window, at
+    window 1: the single visible key becomes two."""
+    w = workloads.make("PA").replace(window=1)
+    ref = oracle.decode(w)
+    assert red(ref, oracle.decode(w.replace(window=2)))
+
+
+# ---- merge and counter protocol (plain f32 model of the GPU's merge) ----
+
+def merge_model(m, l, o, order):
+    """Merge S partials of one output: M = max m over non-empty splits,
+    w = exp2(m - M), num / den summed as 8 interleaved groups in the given
+    group-internal order, groups added in order (all f32)."""
+    f = np.float32
+    S = len(m)
+    live = l > 0
+    M = np.max(np.where(live, m, -np.inf)).astype(f)
+    w = np.where(live, np.exp2((m - M).astype(f)), f(0)).astype(f)
+    num = np.zeros(o.shape[1], f)
+    den = f(0)
+    for g in range(8):
+        idx = list(range(g, S, 8))
+        if order == "reversed":
+            idx = idx[::-1]
+        ng = np.zeros(o.shape[1], f)
+        dg = f(0)
+        for s in idx:
+            if w[s] != 0:
+                ng = (w[s] * o[s] + ng).astype(f)
+                dg = f(w[s] * l[s] + dg)
+        num = (num + ng).astype(f)
+        den = f(den + dg)
+    return (num / den).astype(f)
+
+
+def test_merge_order_reversed_in_one_mode_is_caught():
+    rng = np.random.default_rng(11)
+    S, hd = 64, 256
+    m = rng.normal(0, 3, S).astype(np.float32)
+    l = rng.uniform(0.5, 20, S).astype(np.float32)
+    o = (rng.normal(0, 1, (S, hd)) * l[:, None]).astype(np.float32)
+    a = merge_model(m, l, o, "forward")
+    b = merge_model(m, l, o, "reversed")
+    assert np.allclose(a, b, rtol=1e-5)  # the same value ...
+    assert not np.array_equal(a.view(np.uint32), b.view(np.uint32))  # ... but not the same bits
+
+
+def counter_protocol(counter, splits, reset):
+    """One fused call: every split takes a ticket; the one drawing splits-1
+    merges and (if reset) restores the counter.  Returns (merged, counter)."""
+    merged = False
+    for _ in range(splits):
+        ticket = counter
+        counter += 1
+        if ticket == splits - 1:
+            merged = True
+            if reset:
+                counter = 0
+    return merged, counter
+
+
+def test_missing_counter_reset_is_caught():
+    c = 0
+    for call in range(2):
+        merged, c = counter_protocol(c, 7, reset=True)
+        assert merged and c == 0
+    c = 0
+    merged1, c = counter_protocol(c, 7, reset=False)
+    merged2, c = counter_protocol(c, 7, reset=False)
+    assert merged1 and not merged2 and c != 0  # second call never merges; counters not zero
