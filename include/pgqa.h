@@ -101,9 +101,17 @@ int32_t pgqa_counter_capacity(void);
  *   splits      1..PGQA_MAX_SPLITS, normally from pgqa_choose_splits
  *   counters    NULL: a separate combine kernel merges the splits.  Non-NULL:
  *               int32 [pgqa_counter_capacity()], all zero before the first
- *               call; the last workgroup of each merge unit merges and resets
- *               its counter, so the buffer is all zero again when the call
- *               completes and can be reused without clearing.
+ *               call, and the merge happens inside the decode launch: the last
+ *               workgroup of each merge unit merges and resets its counter;
+ *               when one unit's merge would read 2 MB or more of partials and
+ *               the whole grid fits on the device at once, the launch is
+ *               cooperative instead, and every workgroup merges a share after
+ *               a grid barrier kept (and reset) in the first two counters.
+ *               Either way the buffer is all zero again when the call
+ *               completes and can be reused without clearing.  The result is
+ *               the same as with NULL counters, bit for bit.  For calls with
+ *               one or two merge units and many splits the separate combine
+ *               kernel is the faster choice.
  *   page_map    NULL, or int32 indexed by block-table entries (see above)
  *   stream      hipStream_t
  *

@@ -74,6 +74,7 @@ struct DecodeArgs {
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
   int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
+  int coop;       // shared-page kernel, fused merge: cooperative launch, grid barrier, merge by every workgroup
 };
 
 // Orders this wave's LDS accesses around the point (a wave executes its LDS
@@ -146,6 +147,9 @@ __device__ __forceinline__ s16x4 pack_weights(float p0, float p1, float p2, floa
 __device__ __forceinline__ void store_coherent(float *p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+struct LoadPlain {
+  __device__ __forceinline__ float operator()(const float *p) const { return *p; }
+};
 struct LoadCoherent {
   __device__ __forceinline__ float operator()(const float *p) const {
     return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
@@ -711,6 +715,113 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]), &s_is_last);
 }
 
+// ---- merge of one chunk of 32 hd elements of one (row, query head) ----
+// 256 threads: thread (g, e) = (tid / 32, tid % 32) owns element e of the
+// chunk for the splits s = g mod 8.  Every load -- the (m, l) of all splits
+// and the thread's partial elements -- is issued before any is used, so the
+// merge costs one memory round trip.  Both the combine kernel and the
+// cooperative fused merge run exactly this per element.  `live` false: the
+// threads only take part in the barriers.
+constexpr int kCombineSplits = kMaxSplits / kMergeGroups;  // splits per thread
+struct ChunkScratch {
+  float w[kMaxSplits], l[kMaxSplits], red[kWaves], dgrp[kMergeGroups];
+  float acc[kMergeGroups][32];
+};
+template <class Load>
+__device__ __forceinline__ void merge_chunk32(const DecodeArgs &a, Load ld, int64_t th, int d0, int hd, int tid,
+                                              bool live_chunk, ChunkScratch &cs) {
+  const int g = tid >> 5, e = tid & 31;
+  const int S = a.splits;
+  const float *ml = a.part_ml + th * S * 2;
+  const float *o = a.part_o + th * S * hd + d0 + e;
+  float m = 0.f, l = 0.f;
+  float v[kCombineSplits];
+  if (live_chunk) {
+    const int sm = min(tid, S - 1);
+    m = ld(ml + 2 * sm);
+    l = ld(ml + 2 * sm + 1);
+#pragma unroll
+    for (int i = 0; i < kCombineSplits; ++i) v[i] = ld(o + static_cast<int64_t>(min(g + kMergeGroups * i, S - 1)) * hd);
+  }
+  const bool live = live_chunk && tid < S && l > 0.f;
+  float mx = live ? m : -INFINITY;
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  if ((tid & 63) == 0) cs.red[tid >> 6] = mx;
+  __syncthreads();
+  mx = fmaxf(fmaxf(cs.red[0], cs.red[1]), fmaxf(cs.red[2], cs.red[3]));
+  cs.w[tid] = live ? fast_exp2(m - mx) : 0.f;
+  cs.l[tid] = l;
+  __syncthreads();
+  if (tid < kMergeGroups) {
+    float dg = 0.f;
+    for (int s = tid; s < S; s += kMergeGroups) {
+      const float ws = cs.w[s];
+      dg = ws != 0.f ? __builtin_fmaf(ws, cs.l[s], dg) : dg;
+    }
+    cs.dgrp[tid] = dg;
+  }
+  float num = 0.f;
+  if (live_chunk) {
+#pragma unroll
+    for (int i = 0; i < kCombineSplits; ++i) {
+      const int s = g + kMergeGroups * i;
+      if (s < S) {
+        const float ws = cs.w[s];
+        num = ws != 0.f ? __builtin_fmaf(ws, v[i], num) : num;
+      }
+    }
+  }
+  cs.acc[g][e] = num;
+  __syncthreads();
+  if (live_chunk && tid < 32) {
+    float n = 0.f, den = 0.f;
+#pragma unroll
+    for (int gg = 0; gg < kMergeGroups; ++gg) {
+      n += cs.acc[gg][tid];
+      den += cs.dgrp[gg];
+    }
+    a.out[th * hd + d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
+  }
+  __syncthreads();  // the scratch is reused by the next chunk
+}
+
+// Separate merge: one workgroup per (row, query head, 32 hd elements).
+__global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, int hd) {
+  __shared__ ChunkScratch cs;
+  const int chunks = hd / 32;
+  const int64_t th = blockIdx.x / chunks;
+  const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
+  merge_chunk32(a, LoadPlain{}, th, d0, hd, threadIdx.x, true, cs);
+}
+
+// ---- grid barrier of a cooperative launch (every workgroup resident) ----
+// Two counters of the merge-counter buffer: arrivals, then departures; the
+// last workgroup to leave puts both back to zero.  Relaxed agent-scope
+// atomics: the partial stores are written through and complete before a
+// workgroup arrives, and the loads after the barrier are agent-coherent.  The
+// wait is bounded by time (0.2 s on the 100 MHz real-time counter): every
+// wave leaves it even if the launch were not resident as a whole.
+constexpr uint64_t kBarrierTimeoutTicks = 20000000;
+constexpr int64_t kCoopMergeBytes = int64_t(2) << 20;
+__device__ void grid_barrier(int32_t *c, int nblocks) {
+  wait_all_memory();
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    __hip_atomic_fetch_add(&c[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+    while (__hip_atomic_load(&c[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblocks &&
+           __builtin_amdgcn_s_memrealtime() - t_start < kBarrierTimeoutTicks)
+      __builtin_amdgcn_s_sleep(2);
+    const int left = __hip_atomic_fetch_add(&c[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (left == nblocks - 1) {
+      __hip_atomic_store(&c[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_store(&c[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+  __syncthreads();
+}
+
 // ---------------------------------------------------------------------------
 // Shared-page kernel: tiles of up to 64 columns (e.g. 8 rows x 8 heads of one
 // sequence) and every hd-512 tile.  8 waves in two teams of 4; team t takes
@@ -762,6 +873,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   __shared__ float xfer[2 * kWaves][16];
   __shared__ int s_is_last;
   static_assert(sizeof(FusedScratch<kSharedThreads>) <= sizeof(slot0), "merge scratch must fit a ring slot");
+  static_assert(2 * sizeof(ChunkScratch) <= sizeof(slot0), "chunk merge scratch must fit a ring slot");
   static_assert(256 * MCH * 16 <= sizeof(slot0), "team merge round must fit a ring slot");
   // Ring slot I as a direct reference to its own object (no pointer table):
   // the compiler then knows which object every LDS access touches.
@@ -1097,76 +1209,31 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
     }
     __syncthreads();  // the team-merge area (slot 0) is free again
-    if (fused)
+    if (fused && !a.coop)
       fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
                                       reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
     t0 += nrows;
     __syncthreads();  // LDS is reused by the next tile
   }
+  if (a.splits > 1 && a.counters != nullptr && a.coop) {
+    // every workgroup is resident: after one grid barrier all partials are
+    // complete, and each workgroup merges its share of the launch's outputs,
+    // two chunks of 32 elements at a time (one per 256-thread half)
+    grid_barrier(a.counters, static_cast<int>(gridDim.x));
+    ChunkScratch *cs = reinterpret_cast<ChunkScratch *>(slot0);
+    const int half = tid >> 8;
+    const int64_t per_row = HD / 32;
+    const int64_t nchunks = static_cast<int64_t>(a.rows) * a.nh * per_row;
+    for (int64_t c0 = 2 * static_cast<int64_t>(blockIdx.x); c0 < nchunks; c0 += 2 * static_cast<int64_t>(gridDim.x)) {
+      const int64_t c = c0 + half;
+      const bool live = c < nchunks;
+      const int64_t cc = live ? c : c0;
+      merge_chunk32(a, LoadCoherent{}, cc / per_row, static_cast<int>(cc % per_row) * 32, HD, tid & 255, live,
+                    cs[half]);
+    }
+  }
 }
 
-// Separate merge: one workgroup per (row, query head, 32 hd elements).
-// Thread (g, e) = (tid / 32, tid % 32) owns element e of the chunk for the
-// splits s = g mod 8.  Every load -- the (m, l) of all splits and the thread's
-// partial elements -- is issued before any is used, so the merge costs one
-// memory round trip.
-constexpr int kCombineSplits = kMaxSplits / kMergeGroups;  // splits per thread
-__global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, int hd) {
-  __shared__ float w_s[kMaxSplits], l_s[kMaxSplits], red[kWaves], dgrp[kMergeGroups];
-  __shared__ float acc[kMergeGroups][32];
-  const int tid = threadIdx.x;
-  const int g = tid >> 5, e = tid & 31;
-  const int chunks = hd / 32;
-  const int64_t th = blockIdx.x / chunks;
-  const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
-  const int S = a.splits;
-  const float *ml = a.part_ml + th * S * 2;
-  const float *o = a.part_o + th * S * hd + d0 + e;
-  const int sm = min(tid, S - 1);
-  const float m = ml[2 * sm], l = ml[2 * sm + 1];
-  float v[kCombineSplits];
-#pragma unroll
-  for (int i = 0; i < kCombineSplits; ++i) v[i] = o[static_cast<int64_t>(min(g + kMergeGroups * i, S - 1)) * hd];
-
-  const bool live = tid < S && l > 0.f;
-  float mx = live ? m : -INFINITY;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(red[0], red[1]), fmaxf(red[2], red[3]));
-  w_s[tid] = live ? fast_exp2(m - mx) : 0.f;
-  l_s[tid] = l;
-  __syncthreads();
-  if (tid < kMergeGroups) {
-    float dg = 0.f;
-    for (int s = tid; s < S; s += kMergeGroups) {
-      const float ws = w_s[s];
-      dg = ws != 0.f ? __builtin_fmaf(ws, l_s[s], dg) : dg;
-    }
-    dgrp[tid] = dg;
-  }
-  float num = 0.f;
-#pragma unroll
-  for (int i = 0; i < kCombineSplits; ++i) {
-    const int s = g + kMergeGroups * i;
-    if (s < S) {
-      const float ws = w_s[s];
-      num = ws != 0.f ? __builtin_fmaf(ws, v[i], num) : num;
-    }
-  }
-  acc[g][e] = num;
-  __syncthreads();
-  if (tid < 32) {
-    float n = 0.f, den = 0.f;
-#pragma unroll
-    for (int gg = 0; gg < kMergeGroups; ++gg) {
-      n += acc[gg][tid];
-      den += dgrp[gg];
-    }
-    a.out[th * hd + d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
-  }
-}
 
 thread_local char g_error[512] = "";
 
@@ -1208,27 +1275,58 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
   return p;
 }
 
+// Workgroups of pgqa_shared_kernel<HD, NSL> that the current device holds at
+// once (0 if it cannot launch cooperatively); computed once per device.
+template <int HD, int NSL>
+int64_t coop_capacity() {
+  constexpr int kMaxDevices = 64;
+  static int64_t cap[kMaxDevices];
+  static bool known[kMaxDevices];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
+  if (!known[dev]) {
+    int coop = 0, cus = 0, per_cu = 0;
+    int64_t c = 0;
+    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
+        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pgqa_shared_kernel<HD, NSL>),
+                                                     kSharedThreads, 0) == hipSuccess)
+      c = static_cast<int64_t>(cus) * per_cu;
+    cap[dev] = c;
+    known[dev] = true;
+  }
+  return cap[dev];
+}
+
+template <int HD, int NSL>
+hipError_t launch_shared(DecodeArgs a, int64_t blocks, bool want_coop, hipStream_t stream) {
+  const dim3 grid(static_cast<unsigned>(blocks)), block(kSharedThreads);
+  a.coop = want_coop && blocks <= coop_capacity<HD, NSL>();
+  if (a.coop) {
+    void *args[] = {&a};
+    if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(pgqa_shared_kernel<HD, NSL>), grid, block, args, 0,
+                                   stream) == hipSuccess)
+      return hipSuccess;
+    (void)hipGetLastError();  // refused (e.g. the device is shared): launch it the ordinary way
+    a.coop = 0;
+  }
+  hipLaunchKernelGGL((pgqa_shared_kernel<HD, NSL>), grid, block, 0, stream, a);
+  return hipGetLastError();
+}
+
+// want_coop: a fused merge was asked for; the shared-page kernel then merges
+// cooperatively when its whole grid fits on the device at once.
 template <int HD>
-hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, bool want_coop, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if constexpr (HD >= 128) {
     if (p.kind == 1) {
-      const dim3 sblock(kSharedThreads);
-      if (p.nsl == 2) {
-        hipLaunchKernelGGL((pgqa_shared_kernel<HD, 2>), grid, sblock, 0, stream, a);
-        return hipGetLastError();
-      }
+      if (p.nsl == 2) return launch_shared<HD, 2>(a, blocks, want_coop, stream);
       if constexpr (HD < 512) {
-        if (p.nsl == 1) {
-          hipLaunchKernelGGL((pgqa_shared_kernel<HD, 1>), grid, sblock, 0, stream, a);
-          return hipGetLastError();
-        }
+        if (p.nsl == 1) return launch_shared<HD, 1>(a, blocks, want_coop, stream);
       }
       if constexpr (HD >= 256) {
-        if (p.nsl == 4) {
-          hipLaunchKernelGGL((pgqa_shared_kernel<HD, 4>), grid, sblock, 0, stream, a);
-          return hipGetLastError();
-        }
+        if (p.nsl == 4) return launch_shared<HD, 4>(a, blocks, want_coop, stream);
       }
       return hipErrorInvalidValue;
     }
@@ -1336,13 +1434,19 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   // at once, so that the order of dispatch decides how the launch ends.
   a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
 
+  a.coop = 0;
+  // The last-workgroup merge of one unit reads splits * cap * hd floats.  From
+  // 2 MB up, one workgroup is too slow for that, and a cooperative launch
+  // (about 10 us more launch latency, then every workgroup merges a share)
+  // wins.
+  const bool want_coop = counters != nullptr && splits > 1 && splits * plan.cap * hd * 4 >= kCoopMergeBytes;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   switch (hd) {
-    case 64: err = launch_decode<64>(a, plan, blocks, st); break;
-    case 128: err = launch_decode<128>(a, plan, blocks, st); break;
-    case 256: err = launch_decode<256>(a, plan, blocks, st); break;
-    default: err = launch_decode<512>(a, plan, blocks, st); break;
+    case 64: err = launch_decode<64>(a, plan, blocks, want_coop, st); break;
+    case 128: err = launch_decode<128>(a, plan, blocks, want_coop, st); break;
+    case 256: err = launch_decode<256>(a, plan, blocks, want_coop, st); break;
+    default: err = launch_decode<512>(a, plan, blocks, want_coop, st); break;
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {
