@@ -3,9 +3,11 @@
 One step = one ``pgqa_attn_decode`` call (split-partial kernel plus its merge)
 over one batch of synthetic, seeded inputs already resident in HBM.  The
 default workload is the batched decode: 64 sequences x 1 query row, lengths
-uniform in [512, 16384], nh=32, nkv=8, hd=128, global causal (about 2.2 GB of
-K/V).  Prints one JSON line on stdout; extra per-configuration lines go to
-stderr with --all.
+uniform in [512, 16384], nh=32, nkv=8, hd=128, global causal (about 2.3 GB of
+K/V), the largest of the configurations and one of the long-context ones.
+Prints one JSON line on stdout; it also carries short runs of the other target
+configurations ("secondary"); --all prints every configuration to stderr.
+Caches are evicted between timed steps by a read-only pass over 1 GiB.
 
 Metric: effective KV bandwidth = algorithmic K/V bytes / time, where every
 visible key is counted once per (sequence, kv head): |union of the rows'
@@ -182,6 +184,8 @@ def main():
     ap.add_argument("--no-flush", action="store_true",
                     help="do not evict L2 and the Infinity Cache between timed steps")
     ap.add_argument("--all", action="store_true", help="also time the other configs (stderr)")
+    ap.add_argument("--no-secondary", action="store_true",
+                    help="skip the short runs of the other target configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
@@ -223,6 +227,22 @@ def main():
             log("[bench] " + json.dumps(r))
             torch.cuda.empty_cache()
 
+    # Short runs of the other target configurations, each with the merge mode
+    # that suits it: the local sliding layer (C2, launch-bound), and the two
+    # 128 MiB single-sequence reads (C3, C5), whose one or two merge units
+    # favour the separate combine kernel.
+    secondary = {}
+    if not args.no_secondary:
+        for name, mode in (("C2", "fused"), ("C3", "separate"), ("C5W0", "separate")):
+            if name == args.config:
+                continue
+            r = run_config(name, 20, 3, mode, 0, not args.no_flush)
+            r.pop("_w"), r.pop("_out")
+            secondary[name] = {"splits": r["splits"], "merge": mode, "us_per_call": round(r["kernel_ms_mean"] * 1e3, 2),
+                               "GB/s": round(r["eff_gbs"], 1), "frac": round(r["eff_gbs"] / HBM_PEAK_GBS, 4),
+                               "rows_per_s": round(r["rows_per_s"], 1)}
+            torch.cuda.empty_cache()
+
     ms = res["kernel_ms_mean"]
     traffic = committed_traffic(args.config)
     line = {
@@ -249,6 +269,8 @@ def main():
     }
     if "rel_rms_sample" in res:
         line["rel_rms_sample"] = res["rel_rms_sample"]
+    if secondary:
+        line["secondary"] = secondary
     print(json.dumps(line), flush=True)
 
 
