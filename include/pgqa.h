@@ -135,6 +135,57 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool,
                      int64_t hd, int64_t window, int64_t splits, int32_t *counters,
                      const int32_t *page_map, void *stream);
 
+/*
+ * Rows per prefill tile (span-02 test page, `run()`, the prefill section: the
+ * `prefill_rows_per_tile(hd)` argument of `make_tiles`).  64 for every
+ * supported hd (the kernels cut a tile further into the rows they hold at
+ * once); 0 for an unsupported hd.
+ */
+int32_t pgqa_prefill_rows_per_tile(int64_t hd);
+
+/*
+ * Prefill tiles from the rows' page origins (span-02 test page, `run()`: the
+ * `make_tiles` call).  HOST pointers.  Consecutive rows with equal origin
+ * form runs; each run is cut into tiles of at most rows_per_tile rows.  Tile
+ * n covers rows tile_row0[n] .. tile_row0[n] + tile_rows[n] - 1.
+ *   page_origin  int32 [rows]      (host)
+ *   rows_per_tile 1 .. pgqa_prefill_rows_per_tile(hd)
+ *   tile_row0, tile_rows  int32 [capacity]  (host, written)
+ * Returns the number of tiles, PGQA_EINVAL for bad arguments, or PGQA_ECAP
+ * when more than `capacity` tiles would be needed.
+ */
+int64_t pgqa_make_tiles(const int32_t *page_origin, int64_t rows, int64_t rows_per_tile, int32_t *tile_row0,
+                        int32_t *tile_rows, int64_t capacity);
+
+/*
+ * Paged prefill attention (span-02 test page, `run()`: the `attn_prefill`
+ * calls, checked against the same `reference` as decode with every context
+ * row causal).  Computes exactly what pgqa_attn_decode computes for the same
+ * rows (same visibility rule, pool addressing, page map and rounding), with
+ * the rows grouped by the caller's tiles instead of split across KV: each
+ * (tile, kv head) is one pass over the tile's pages, with no partials.
+ * Arguments as for pgqa_attn_decode, plus:
+ *   tile_row0, tile_rows  int32 [ntiles] DEVICE arrays, normally from
+ *                pgqa_make_tiles: every tile's rows share one page origin,
+ *                1 <= tile_rows[n] <= pgqa_prefill_rows_per_tile(hd), and
+ *                the tiles cover rows 0 .. rows - 1 without overlap.  A tile
+ *                reaching outside 0 .. rows - 1 is skipped; a tile whose rows
+ *                change origin is cut at the change (rows after it are not
+ *                written).
+ *   ntiles       1 .. rows
+ *   rows         query rows (q and out hold rows * nh * hd values); the
+ *                page's call leaves it implicit in the tiles.
+ * No partial buffer, no counters, no split count.  The result equals
+ * pgqa_attn_decode's for the same rows within the rel-RMS bound (not bit for
+ * bit: decode may group rows and split keys differently), and is bit for bit
+ * the same for an identity pool and a permuted pool behind a page map.
+ * Returns PGQA_OK, PGQA_EINVAL or PGQA_ELAUNCH.
+ */
+int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                      const int32_t *page_origin, const int32_t *qpos, const int32_t *kv_last,
+                      const int32_t *tile_row0, const int32_t *tile_rows, int64_t ntiles, int64_t rows, int64_t nh,
+                      int64_t nkv, int64_t hd, int64_t window, const int32_t *page_map, void *stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pgqa_last_error(void);
 

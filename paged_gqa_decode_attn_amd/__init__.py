@@ -8,7 +8,8 @@ CPU or framework fallback, and a missing library is an error.
 
 Entry points (same names and argument order as the C ABI, after the span-02
 GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
-``counter_capacity``, ``attn_decode``.
+``counter_capacity``, ``attn_decode``, ``prefill_rows_per_tile``,
+``make_tiles``, ``attn_prefill``.
 """
 from __future__ import annotations
 
@@ -52,6 +53,12 @@ def lib() -> ctypes.CDLL:
         h.pgqa_attn_decode.restype = ctypes.c_int
         h.pgqa_attn_decode.argtypes = [p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64,
                                        p, p, p]
+        h.pgqa_prefill_rows_per_tile.restype = ctypes.c_int32
+        h.pgqa_prefill_rows_per_tile.argtypes = [i64]
+        h.pgqa_make_tiles.restype = ctypes.c_int64
+        h.pgqa_make_tiles.argtypes = [p, i64, i64, p, p, i64]
+        h.pgqa_attn_prefill.restype = ctypes.c_int
+        h.pgqa_attn_prefill.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
         _lib = h
     return _lib
 
@@ -130,5 +137,55 @@ def attn_decode(out, part, q, k_pool, v_pool, block_table, page_origin, qpos, kv
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     rc = lib().pgqa_attn_decode(*args, rows, nh, nkv, hd, window, splits, cnt, pm, stream)
+    if rc != OK:
+        raise PgqaError(rc, last_error())
+
+
+def prefill_rows_per_tile(hd: int) -> int:
+    return int(lib().pgqa_prefill_rows_per_tile(hd))
+
+
+def make_tiles(page_origin, rows_per_tile: int):
+    """Prefill tiles from host page origins: (tile_row0, tile_rows) int32 numpy arrays."""
+    import numpy as np
+
+    org = np.ascontiguousarray(page_origin, dtype=np.int32)
+    n = len(org)
+    t0 = np.zeros(max(n, 1), np.int32)
+    tn = np.zeros(max(n, 1), np.int32)
+    rc = lib().pgqa_make_tiles(org.ctypes.data, n, rows_per_tile, t0.ctypes.data, tn.ctypes.data, len(t0))
+    if rc < 0:
+        raise PgqaError(int(rc), last_error())
+    return t0[:rc].copy(), tn[:rc].copy()
+
+
+def attn_prefill(out, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last, tile_row0, tile_rows,
+                 ntiles: int, rows: int, nh: int, nkv: int, hd: int, window: int, page_map=None,
+                 stream=None) -> None:
+    """Enqueue one prefill call (see ``pgqa_attn_prefill`` in include/pgqa.h).
+    ``tile_row0`` / ``tile_rows`` are int32 device tensors of ``ntiles``."""
+    import torch
+
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    i32 = (torch.int32,)
+    n_out = rows * nh * hd
+    args = [
+        _addr(out, "out", b16, n_out),
+        _addr(q, "q", b16, n_out),
+        _addr(k_pool, "k_pool", b16),
+        _addr(v_pool, "v_pool", b16),
+        _addr(block_table, "block_table", i32),
+        _addr(page_origin, "page_origin", i32, rows),
+        _addr(qpos, "qpos", i32, rows),
+        _addr(kv_last, "kv_last", i32, rows),
+        _addr(tile_row0, "tile_row0", i32, ntiles),
+        _addr(tile_rows, "tile_rows", i32, ntiles),
+    ]
+    pm = _addr(page_map, "page_map", i32)
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device if hasattr(out, "device") else None).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = lib().pgqa_attn_prefill(*args, ntiles, rows, nh, nkv, hd, window, pm, stream)
     if rc != OK:
         raise PgqaError(rc, last_error())

@@ -75,6 +75,12 @@ struct DecodeArgs {
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
   int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
   int coop;       // shared-page kernel, fused merge: cooperative launch, grid barrier, merge by every workgroup
+  // prefill: caller-made tiles (runs of rows on one sequence, at most
+  // kPrefillRowsPerTile rows each), cut into nsub sub-tiles of rmax rows;
+  // NULL for decode
+  const int32_t *tile_row0;
+  const int32_t *tile_nrows;
+  int ntiles, nsub;
 };
 
 // Orders this wave's LDS accesses around the point (a wave executes its LDS
@@ -208,17 +214,26 @@ struct Tile {
   int fp0, fp1;  // pages [fp0, fp1) are visible in full to every row of the tile
   bool lead;
 };
-__device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane) {
+// With force_rows > 0 (prefill) the tile is rows t0 .. t0 + force_rows - 1 as
+// the caller cut them, shortened to the run that shares row t0's origin.
+__device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane, int force_rows = 0) {
   Tile t;
-  const bool lrow = lane < a.rmax && t0 + lane < a.rows;
+  const int span = force_rows > 0 ? force_rows : a.rmax;
+  const bool lrow = lane < span && t0 + lane < a.rows;
   const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
   const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
   t.hi_l = lrow ? a.kv_last[t0 + lane] : -1;
-  const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
   t.origin = __builtin_amdgcn_readfirstlane(org_l);
-  t.lead = t0 % a.rmax == 0 || prev_origin != t.origin;
-  const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin || (t0 + lane) % a.rmax == 0));
-  t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
+  if (force_rows > 0) {
+    t.lead = true;
+    const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin));
+    t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
+  } else {
+    const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
+    t.lead = t0 % a.rmax == 0 || prev_origin != t.origin;
+    const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin || (t0 + lane) % a.rmax == 0));
+    t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
+  }
   t.lo_l = a.window > 0 ? max(0, qp_l + 1 - a.window) : 0;
   const bool live = lane < t.nrows && t.hi_l >= t.lo_l;
   int lo = live ? t.lo_l : INT_MAX, hi = live ? t.hi_l : -1;
@@ -240,6 +255,18 @@ __device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane)
   t.fp0 = (lo_all + kPage - 1) / kPage;
   t.fp1 = hi_all >= lo_all ? (hi_all + 1) / kPage : t.fp0;
   return t;
+}
+
+// Prefill: sub-tile p of the launch -> its first row and row count (0: none,
+// also for a caller tile that would reach outside rows 0 .. rows - 1).
+constexpr int kPrefillRowsPerTile = 64;
+__device__ __forceinline__ int prefill_subtile(const DecodeArgs &a, int p, int &nrows) {
+  const int i = p / a.nsub, j = p - i * a.nsub;
+  const int r0 = a.tile_row0[i], n = a.tile_nrows[i];
+  nrows = 0;
+  if (r0 < 0 || n < 1 || n > kPrefillRowsPerTile || r0 > a.rows - n) return 0;
+  nrows = max(0, min(a.rmax, n - j * a.rmax));
+  return r0 + j * a.rmax;
 }
 
 // The row of rank p when the rows are ordered by decreasing visible length
@@ -438,7 +465,9 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   const int hb = b % a.hblocks;
   b /= a.hblocks;
   const int kh = b % a.nkv;
-  const int t0 = row_of_rank(a, b / a.nkv, lane);
+  int sub_rows = 0;
+  const int t0 = a.tile_row0 ? prefill_subtile(a, b / a.nkv, sub_rows) : row_of_rank(a, b / a.nkv, lane);
+  if (a.tile_row0 && sub_rows == 0) return;
 
   // ---- tile; Q for every possible column is requested in the same round ----
   const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
@@ -456,7 +485,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
       }
     }
   }
-  const Tile tile = tile_rows(a, t0, lane);
+  const Tile tile = tile_rows(a, t0, lane, sub_rows);
   if (!tile.lead) return;
   const int origin = tile.origin;
   const int nrows = tile.nrows;
@@ -907,10 +936,16 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   const int kh = b % a.nkv;
   // this workgroup's rmax-aligned block of rows; it takes the block's tiles
   // (runs of rows on one sequence) one after another
-  const int rb0 = (b / a.nkv) * a.rmax;
-  const int rb1 = min(rb0 + a.rmax, a.rows);
+  // (prefill: one caller-made sub-tile)
+  int sub_rows = 0;
+  int rb0 = (b / a.nkv) * a.rmax;
+  int rb1 = min(rb0 + a.rmax, a.rows);
+  if (a.tile_row0) {
+    rb0 = prefill_subtile(a, b / a.nkv, sub_rows);
+    rb1 = sub_rows > 0 ? rb0 + 1 : rb0;
+  }
   for (int t0 = rb0; t0 < rb1;) {
-    const Tile tile = tile_rows(a, t0, lane);
+    const Tile tile = tile_rows(a, t0, lane, sub_rows);
     const int nrows = tile.nrows;
     int pbeg, pend;
     split_range(tile, split, a.splits, pbeg, pend);
@@ -1277,6 +1312,19 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
 
 // Workgroups of pgqa_shared_kernel<HD, NSL> that the current device holds at
 // once (0 if it cannot launch cooperatively); computed once per device.
+// Prefill: tiles have many rows, so the shared-page kernel takes every hd
+// from 128 up with 64-column tiles (32 at hd 512), reading each page once per
+// 64 columns; hd 64 keeps the per-wave kernel's 16-column tiles.
+Plan make_prefill_plan(int64_t group, int64_t hd) {
+  Plan p;
+  p.kind = hd >= 128 ? 1 : 0;
+  p.nsl = p.kind == 1 ? (hd == 512 ? 2 : 1) : 1;
+  p.cap = p.kind == 1 ? 16 * (kWaves / p.nsl) : 16;
+  p.rmax = group <= p.cap ? static_cast<int>(p.cap / group) : 1;
+  p.hblocks = group <= p.cap ? 1 : static_cast<int>((group + p.cap - 1) / p.cap);
+  return p;
+}
+
 template <int HD, int NSL>
 int64_t coop_capacity() {
   constexpr int kMaxDevices = 64;
@@ -1429,6 +1477,10 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   a.rmax = plan.rmax;
   a.hblocks = plan.hblocks;
   a.cap = plan.cap;
+  a.tile_row0 = nullptr;
+  a.tile_nrows = nullptr;
+  a.ntiles = 0;
+  a.nsub = 0;
   // Ordering rows costs a dependent memory round trip before a workgroup can
   // start; it pays only when the launch is several times what the GPU holds
   // at once, so that the order of dispatch decides how the launch ends.
@@ -1455,6 +1507,95 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
     err = hipGetLastError();
     if (err != hipSuccess) return fail(PGQA_ELAUNCH, "combine kernel launch: %s", hipGetErrorString(err));
   }
+  return PGQA_OK;
+}
+
+int32_t pgqa_prefill_rows_per_tile(int64_t hd) {
+  return hd == 64 || hd == 128 || hd == 256 || hd == 512 ? kPrefillRowsPerTile : 0;
+}
+
+int64_t pgqa_make_tiles(const int32_t *page_origin, int64_t rows, int64_t rows_per_tile, int32_t *tile_row0,
+                        int32_t *tile_rows, int64_t capacity) {
+  g_error[0] = '\0';
+  if (!page_origin || !tile_row0 || !tile_rows || rows < 0 || rows > INT_MAX || rows_per_tile < 1 ||
+      rows_per_tile > kPrefillRowsPerTile)
+    return fail(PGQA_EINVAL, "make_tiles: bad arguments");
+  int64_t n = 0;
+  for (int64_t r = 0; r < rows;) {
+    int64_t e = r + 1;
+    while (e < rows && e - r < rows_per_tile && page_origin[e] == page_origin[r]) ++e;
+    if (n >= capacity) return fail(PGQA_ECAP, "make_tiles: more than %lld tiles", (long long)capacity);
+    tile_row0[n] = static_cast<int32_t>(r);
+    tile_rows[n] = static_cast<int32_t>(e - r);
+    ++n;
+    r = e;
+  }
+  return n;
+}
+
+int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *v_pool, const int32_t *block_table,
+                      const int32_t *page_origin, const int32_t *qpos, const int32_t *kv_last,
+                      const int32_t *tile_row0, const int32_t *tile_rows, int64_t ntiles, int64_t rows, int64_t nh,
+                      int64_t nkv, int64_t hd, int64_t window, const int32_t *page_map, void *stream) {
+  g_error[0] = '\0';
+  if (!out || !q || !k_pool || !v_pool || !block_table || !page_origin || !qpos || !kv_last || !tile_row0 ||
+      !tile_rows)
+    return fail(PGQA_EINVAL, "a required pointer is NULL");
+  if (rows < 1 || rows > INT_MAX / 2) return fail(PGQA_EINVAL, "rows=%lld out of range", (long long)rows);
+  if (ntiles < 1 || ntiles > rows) return fail(PGQA_EINVAL, "ntiles=%lld out of range", (long long)ntiles);
+  if (nh < 1 || nkv < 1 || nh % nkv != 0 || nh > 65536)
+    return fail(PGQA_EINVAL, "nh=%lld must be a positive multiple of nkv=%lld", (long long)nh, (long long)nkv);
+  if (hd != 64 && hd != 128 && hd != 256 && hd != 512)
+    return fail(PGQA_EINVAL, "hd=%lld unsupported (64, 128, 256 or 512)", (long long)hd);
+  if (window < 0 || window > INT_MAX) return fail(PGQA_EINVAL, "window=%lld out of range", (long long)window);
+  if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15u)
+    return fail(PGQA_EINVAL, "q and the pools must be 16-byte aligned");
+  if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(PGQA_EINVAL, "out must be 2-byte aligned");
+
+  const int64_t group = nh / nkv;
+  const Plan plan = make_prefill_plan(group, hd);
+  const int64_t nsub = (kPrefillRowsPerTile + plan.rmax - 1) / plan.rmax;
+  const int64_t blocks = ntiles * nsub * nkv * plan.hblocks;
+  if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
+
+  DecodeArgs a;
+  a.out = static_cast<uint16_t *>(out);
+  a.part_o = nullptr;
+  a.part_ml = nullptr;
+  a.q = static_cast<const uint16_t *>(q);
+  a.k_pool = static_cast<const uint16_t *>(k_pool);
+  a.v_pool = static_cast<const uint16_t *>(v_pool);
+  a.block_table = block_table;
+  a.page_origin = page_origin;
+  a.qpos = qpos;
+  a.kv_last = kv_last;
+  a.counters = nullptr;
+  a.page_map = page_map;
+  a.rows = static_cast<int>(rows);
+  a.nh = static_cast<int>(nh);
+  a.nkv = static_cast<int>(nkv);
+  a.group = static_cast<int>(group);
+  a.window = static_cast<int>(window);
+  a.splits = 1;
+  a.rmax = plan.rmax;
+  a.hblocks = plan.hblocks;
+  a.cap = plan.cap;
+  a.rank_rows = 0;
+  a.coop = 0;
+  a.tile_row0 = tile_row0;
+  a.tile_nrows = tile_rows;
+  a.ntiles = static_cast<int>(ntiles);
+  a.nsub = static_cast<int>(nsub);
+
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  hipError_t err;
+  switch (hd) {
+    case 64: err = launch_decode<64>(a, plan, blocks, false, st); break;
+    case 128: err = launch_decode<128>(a, plan, blocks, false, st); break;
+    case 256: err = launch_decode<256>(a, plan, blocks, false, st); break;
+    default: err = launch_decode<512>(a, plan, blocks, false, st); break;
+  }
+  if (err != hipSuccess) return fail(PGQA_ELAUNCH, "prefill kernel launch: %s", hipGetErrorString(err));
   return PGQA_OK;
 }
 

@@ -48,6 +48,21 @@ class DeviceWorkload:
             torch.cuda.synchronize()
         return out
 
+    def prefill(self, tiles=None, out=None, sync=True):
+        """One pgqa_attn_prefill call over all rows; tiles default to
+        make_tiles(page_origin, prefill_rows_per_tile(hd))."""
+        w = self.w
+        if tiles is None:
+            tiles = pg.make_tiles(w.page_origin, pg.prefill_rows_per_tile(w.hd))
+        t0, tn = dev_i32(tiles[0]), dev_i32(tiles[1])
+        if out is None:
+            out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
+        pg.attn_prefill(out, self.q, self.k, self.v, self.bt, self.off, self.qpos, self.last, t0, tn,
+                        len(tiles[0]), w.rows, w.nh, w.nkv, w.hd, w.window, self.pmap)
+        if sync:
+            torch.cuda.synchronize()
+        return out
+
     def host(self, out):
         return out.cpu().numpy().view(np.uint16)
 

@@ -103,3 +103,72 @@ def test_missing_library_is_loud(tmp_path, monkeypatch):
     monkeypatch.setattr(pg, "_lib", None)
     with pytest.raises(pg.PgqaError):
         pg.lib()
+
+
+# ---- prefill (host side) ----
+
+def test_prefill_rows_per_tile():
+    for hd in (64, 128, 256, 512):
+        assert pg.prefill_rows_per_tile(hd) == 64
+    assert pg.prefill_rows_per_tile(96) == 0
+
+
+def brute_tiles(origins, rpt):
+    t0, tn = [], []
+    r = 0
+    while r < len(origins):
+        e = r + 1
+        while e < len(origins) and e - r < rpt and origins[e] == origins[r]:
+            e += 1
+        t0.append(r)
+        tn.append(e - r)
+        r = e
+    return t0, tn
+
+
+@pytest.mark.parametrize("origins,rpt", [
+    ([0] * 200, 64),                       # one sequence: full tiles and a ragged one
+    ([0] * 64, 64),                        # exactly one tile
+    ([3], 64),                             # one row
+    ([0, 0, 5, 5, 5, 9, 0, 0], 2),         # runs cut by origin changes and by size
+    ([7] * 10 + [20] * 130 + [1] * 3, 64),
+])
+def test_make_tiles(origins, rpt):
+    t0, tn = pg.make_tiles(origins, rpt)
+    bt0, btn = brute_tiles(origins, rpt)
+    assert t0.tolist() == bt0 and tn.tolist() == btn
+    # the tiles cover every row once, and each tile keeps one origin
+    covered = [r for a, n in zip(t0, tn) for r in range(a, a + n)]
+    assert covered == list(range(len(origins)))
+    for a, n in zip(t0, tn):
+        assert len(set(origins[a:a + n])) == 1 and 1 <= n <= rpt
+
+
+def test_make_tiles_refusals():
+    import numpy as np
+    org = np.zeros(10, np.int32)
+    t0 = np.zeros(2, np.int32)
+    tn = np.zeros(2, np.int32)
+    assert pg.lib().pgqa_make_tiles(org.ctypes.data, 10, 4, t0.ctypes.data, tn.ctypes.data, 2) == pg.ECAP
+    assert pg.lib().pgqa_make_tiles(org.ctypes.data, 10, 0, t0.ctypes.data, tn.ctypes.data, 2) == pg.EINVAL
+    assert pg.lib().pgqa_make_tiles(org.ctypes.data, 10, 65, t0.ctypes.data, tn.ctypes.data, 2) == pg.EINVAL
+    assert pg.lib().pgqa_make_tiles(None, 10, 4, t0.ctypes.data, tn.ctypes.data, 2) == pg.EINVAL
+
+
+def pcall(**kw):
+    a = dict(out=FAKE, q=FAKE, k=FAKE, v=FAKE, bt=FAKE, off=FAKE, qpos=FAKE, last=FAKE, t0=FAKE,
+             tn=FAKE, ntiles=1, rows=1, nh=4, nkv=1, hd=64, window=0, pmap=None)
+    a.update(kw)
+    return pg.lib().pgqa_attn_prefill(a["out"], a["q"], a["k"], a["v"], a["bt"], a["off"], a["qpos"],
+                                      a["last"], a["t0"], a["tn"], a["ntiles"], a["rows"], a["nh"],
+                                      a["nkv"], a["hd"], a["window"], a["pmap"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(out=None), dict(q=None), dict(t0=None), dict(tn=None), dict(last=None),
+    dict(rows=0), dict(ntiles=0), dict(ntiles=2, rows=1), dict(nh=6, nkv=4), dict(hd=32),
+    dict(window=-1), dict(k=FAKE + 4),
+])
+def test_prefill_refusals(kw):
+    assert pcall(**kw) == pg.EINVAL
+    assert pg.last_error() != ""
