@@ -30,6 +30,7 @@ sys.path.insert(0, ROOT)
 import workloads  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E peak
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 matrix peak
 
 
 def log(*a):
@@ -142,6 +143,49 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     return res
 
 
+def prefill_flops(w) -> int:
+    """Algorithmic flops of a prefill: per (row, head), 2 * hd for q.k and
+    2 * hd for p.v over every visible key."""
+    vis = 0
+    for t in range(w.rows):
+        q = int(w.qpos[t])
+        lo = max(0, q + 1 - w.window) if w.window > 0 else 0
+        vis += max(0, int(w.kv_last[t]) - lo + 1)
+    return vis * w.nh * w.hd * 4
+
+
+def run_prefill(w, steps, warmup, flush):
+    """Time pgqa_attn_prefill over every row of w (tiles from make_tiles)."""
+    import torch
+
+    import paged_gqa_decode_attn_amd as pg
+    from tests.gpu_util import DeviceWorkload, dev_i32  # upload helpers only
+
+    dw = DeviceWorkload(w)
+    t0, tn = pg.make_tiles(w.page_origin, pg.prefill_rows_per_tile(w.hd))
+    tiles = (t0, tn)
+    out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.int32, device="cuda") if flush else None
+    sink = torch.zeros((), dtype=torch.int64, device="cuda") if flush else None
+    for _ in range(warmup):
+        dw.prefill(tiles=tiles, out=out, sync=False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, dtype=torch.int64, out=sink)
+        ev[i][0].record(stream)
+        dw.prefill(tiles=tiles, out=out, sync=False)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    fl = prefill_flops(w)
+    return {"rows": w.rows, "us_per_call": round(ms * 1e3, 2), "TFLOP/s": round(fl / (ms * 1e-3) / 1e12, 2),
+            "frac_bf16_mfma": round(fl / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, 4), "flops": fl,
+            "tiles": len(t0)}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload: the first
     n rows, n growing by 4x until a call costs a quarter of the budget; a sample
@@ -241,6 +285,14 @@ def main():
             secondary[name] = {"splits": r["splits"], "merge": mode, "us_per_call": round(r["kernel_ms_mean"] * 1e3, 2),
                                "GB/s": round(r["eff_gbs"], 1), "frac": round(r["eff_gbs"] / HBM_PEAK_GBS, 4),
                                "rows_per_s": round(r["rows_per_s"], 1)}
+            torch.cuda.empty_cache()
+        # paged prefill (MFMA-bound): the page's PA shape, and an 8K-token
+        # causal context of the same head layout
+        for pname, pw in (("prefill_PA", workloads.single_sequence("pfPA", ctx=1500, rows=1500, nh=16, nkv=8,
+                                                                   hd=256, window=1024)),
+                          ("prefill_8k", workloads.single_sequence("pf8k", ctx=8192, rows=8192, nh=16, nkv=8,
+                                                                   hd=256, window=0))):
+            secondary[pname] = run_prefill(pw, 10, 2, not args.no_flush)
             torch.cuda.empty_cache()
 
     ms = res["kernel_ms_mean"]
