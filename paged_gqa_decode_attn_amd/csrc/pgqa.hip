@@ -34,6 +34,7 @@
 //     every window cannot leak into the result.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <climits>
 #include <cstdarg>
 #include <cstdint>
@@ -276,7 +277,7 @@ __device__ __forceinline__ int prefill_subtile(const DecodeArgs &a, int p, int &
 // selection is a binary search on the length with wave-wide counts.  Small
 // launches and batches of more than kRankRows rows keep their own order.
 constexpr int kRankRows = 1024;
-constexpr int64_t kRankMinBlocks = 1024;  // launches this large take rows longest first
+constexpr int64_t kRankMinBlocks = 512;  // launches this large take rows longest first
 constexpr int kRankLenMax = (1 << 30) - 1;  // longer rows rank as equals
 __device__ __forceinline__ int row_of_rank(const DecodeArgs &a, int p, int lane) {
   if (!a.rank_rows || a.rows > kRankRows) return p;
@@ -1396,17 +1397,18 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
   const int64_t units = nseq * nkv;
   const int64_t pages = (kv_span + kPage - 1) / kPage;
-  // Aim at about 6 workgroups per CU on the 256 CUs (with the longest rows
-  // dispatched first, uneven sequence lengths then still balance), with at
-  // least 16 pages in a split of a long span and up to 8 splits of at least 4
-  // pages for a short one.
-  const int64_t target = 1536;
-  int64_t s = (target + units - 1) / units;
-  int64_t smax = pages / 4 < 8 ? pages / 4 : 8;
-  if (pages / 16 > smax) smax = pages / 16;
-  if (smax < 1) smax = 1;
-  if (smax > kMaxSplits) smax = kMaxSplits;
-  if (s > smax) s = smax;
+  // Two regimes, measured over split counts 1..256 on every configuration:
+  //  - long spans are bandwidth-bound: about 6 workgroups per CU on the 256
+  //    CUs (with the longest rows dispatched first, uneven lengths still
+  //    balance), at least 16 pages per split;
+  //  - short spans are latency-bound: about 64 workgroups in all, at least 4
+  //    pages per split.
+  // The larger of the two wins.
+  auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+  const int64_t s_long = std::min(cdiv(1536, units), pages / 16);
+  const int64_t s_short = std::min(cdiv(64, units), pages / 4);
+  int64_t s = std::max(s_long, s_short);
+  if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return static_cast<int32_t>(s);
 }
@@ -1482,8 +1484,9 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   a.ntiles = 0;
   a.nsub = 0;
   // Ordering rows costs a dependent memory round trip before a workgroup can
-  // start; it pays only when the launch is several times what the GPU holds
-  // at once, so that the order of dispatch decides how the launch ends.
+  // start; it pays only when the launch is larger than what the GPU holds at
+  // once (2-3 per-wave workgroups per CU), so that the order of dispatch
+  // decides how the launch ends.
   a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
 
   a.coop = 0;
