@@ -103,15 +103,14 @@ int32_t pgqa_counter_capacity(void);
  *               int32 [pgqa_counter_capacity()], all zero before the first
  *               call, and the merge happens inside the decode launch: the last
  *               workgroup of each merge unit merges and resets its counter;
- *               when one unit's merge would read 2 MB or more of partials and
- *               the whole grid fits on the device at once, the launch is
- *               cooperative instead, and every workgroup merges a share after
- *               a grid barrier kept (and reset) in the first two counters.
- *               Either way the buffer is all zero again when the call
- *               completes and can be reused without clearing.  The result is
- *               the same as with NULL counters, bit for bit.  For calls with
- *               one or two merge units and many splits the separate combine
- *               kernel is the faster choice.
+ *               when one unit's merge would read 2 MB or more of partials, the
+ *               unit's workgroups wait briefly (at most 20 us each) for the
+ *               last one and merge it together, claiming slices through the
+ *               same counter.  Either way the buffer is all zero again when
+ *               the call completes and can be reused without clearing.  The
+ *               result is the same as with NULL counters, bit for bit.  For
+ *               calls with one or two merge units and many splits the
+ *               separate combine kernel is the faster choice.
  *   page_map    NULL, or int32 indexed by block-table entries (see above)
  *   stream      hipStream_t
  *

@@ -75,7 +75,8 @@ struct DecodeArgs {
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
   int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
-  int coop;       // shared-page kernel, fused merge: cooperative launch, grid barrier, merge by every workgroup
+  int spin_ticks;  // shared-page kernel, fused merge: > 0 selects the parallel (claimed-slice) merge and
+                   // bounds each workgroup's wait for the unit's last arrival (100 MHz ticks)
   // prefill: caller-made tiles (runs of rows on one sequence, at most
   // kPrefillRowsPerTile rows each), cut into nsub sub-tiles of rmax rows;
   // NULL for decode
@@ -750,7 +751,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
 // chunk for the splits s = g mod 8.  Every load -- the (m, l) of all splits
 // and the thread's partial elements -- is issued before any is used, so the
 // merge costs one memory round trip.  Both the combine kernel and the
-// cooperative fused merge run exactly this per element.  `live` false: the
+// parallel fused merge run exactly this per element.  `live` false: the
 // threads only take part in the barriers.
 constexpr int kCombineSplits = kMaxSplits / kMergeGroups;  // splits per thread
 struct ChunkScratch {
@@ -825,31 +826,96 @@ __global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, in
   merge_chunk32(a, LoadPlain{}, th, d0, hd, threadIdx.x, true, cs);
 }
 
-// ---- grid barrier of a cooperative launch (every workgroup resident) ----
-// Two counters of the merge-counter buffer: arrivals, then departures; the
-// last workgroup to leave puts both back to zero.  Relaxed agent-scope
-// atomics: the partial stores are written through and complete before a
-// workgroup arrives, and the loads after the barrier are agent-coherent.  The
-// wait is bounded by time (0.2 s on the 100 MHz real-time counter): every
-// wave leaves it even if the launch were not resident as a whole.
-constexpr uint64_t kBarrierTimeoutTicks = 20000000;
-constexpr int64_t kCoopMergeBytes = int64_t(2) << 20;
-__device__ void grid_barrier(int32_t *c, int nblocks) {
-  wait_all_memory();
+// ---- parallel fused merge of one unit (claimed slices) ----
+// The unit's counter word holds arrivals and claims in its low 16 bits and
+// finished slices in its high 16 bits.
+//  1. Every workgroup (partials written through and complete) adds 1: the
+//     workgroup that draws S - 1 is the last to arrive.
+//  2. The others wait for the count to reach S, at most spin_ticks of the
+//     100 MHz real-time counter (or until they see the count below their own
+//     arrival: the unit is merged already); one that gives up leaves without
+//     touching the word again.
+//  3. Every workgroup still present claims slices -- pairs of 32-element
+//     output chunks of the unit -- with fetch-and-add on the low bits
+//     (slice = old count - S) and merges each with the combine kernel's
+//     per-element code.  A claim past the last slice (or after the reset) is
+//     taken back with a subtraction.  The last arrival claims until none are
+//     left, so every slice is merged even if all the others gave up.
+//  4. Each merged slice adds 1 << 16; the workgroup that completes the last
+//     slice subtracts what arrivals, claims and completions added (S +
+//     nslices + (nslices << 16)); claims taken back net to zero, so the word
+//     is zero again for the next call.
+// No workgroup waits on another for more than spin_ticks, and none needs
+// another to be resident: a launch larger than the device holds only merges
+// with fewer helpers.
+constexpr int64_t kParallelMergeBytes = int64_t(2) << 20;  // per-unit partials from which the merge goes parallel
+constexpr int kClaimSpinTicks = 2000;                      // 20 us
+
+// One claimed slice: chunks 2 slice and 2 slice + 1 of the unit's outputs,
+// one per 256-thread half.
+template <int HD>
+__device__ __forceinline__ void merge_slice(const DecodeArgs &a, int t0, int kh, int hb, int nrows,
+                                                      int nchunks, int cap, int slice, ChunkScratch *cs) {
+  constexpr int per_col = HD / 32;
+  const int tid = threadIdx.x;
+  const int half = tid >> 8;
+  const int c = 2 * slice + half;
+  const bool live = c < nchunks;
+  const int cc = live ? c : 2 * slice;
+  const Column rc = tile_column(cc / per_col, a.group, nrows, hb, cap);
+  const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+  merge_chunk32(a, LoadCoherent{}, th, (cc % per_col) * 32, HD, tid & 255, live, cs[half]);
+}
+
+template <int HD, int NT>
+__device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
+                              ChunkScratch *cs, int *s_word) {
+  static_assert(NT == 2 * kThreads, "two chunks per claim: one per 256-thread half");
+  int32_t *w = a.counters + (t0 * a.nkv + kh) * a.hblocks + hb;
+  const int S = a.splits;
+  const int nchunks = ncols * (HD / 32);
+  const int nslices = (nchunks + 1) / 2;
+  const int tid = threadIdx.x;
+  wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
-  if (threadIdx.x == 0) {
-    __hip_atomic_fetch_add(&c[0], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-    while (__hip_atomic_load(&c[0], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < nblocks &&
-           __builtin_amdgcn_s_memrealtime() - t_start < kBarrierTimeoutTicks)
-      __builtin_amdgcn_s_sleep(2);
-    const int left = __hip_atomic_fetch_add(&c[1], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    if (left == nblocks - 1) {
-      __hip_atomic_store(&c[0], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_store(&c[1], 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (tid == 0) {
+    const int t = __hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+    bool ready = t == S - 1;
+    if (!ready) {
+      const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
+      while (!ready && __builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(a.spin_ticks)) {
+        __builtin_amdgcn_s_sleep(2);
+        const int low = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+        if (low <= t) break;
+        ready = low >= S;
+      }
     }
+    *s_word = ready;
   }
   __syncthreads();
+  if (!*s_word) return;
+  for (;;) {
+    __syncthreads();  // everyone has read the previous claim
+    if (tid == 0) {
+      const int low = __hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+      int slice = low - S;
+      if (slice < 0 || slice >= nslices) {
+        __hip_atomic_fetch_sub(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        slice = -1;
+      }
+      *s_word = slice;
+    }
+    __syncthreads();
+    const int slice = *s_word;
+    if (slice < 0) return;
+    merge_slice<HD>(a, t0, kh, hb, nrows, nchunks, cap, slice, cs);
+    __syncthreads();
+    if (tid == 0) {
+      const int done = __hip_atomic_fetch_add(w, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16;
+      if (done == nslices - 1)
+        __hip_atomic_fetch_sub(w, S + nslices + (nslices << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -902,6 +968,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) f32x4 xscore[2 * kWaves][64];  // partial scores per wave
   __shared__ float xfer[2 * kWaves][16];
   __shared__ int s_is_last;
+  __shared__ int3 s_tiles[64];  // tiles whose parallel merge follows the page loop (row, rows, columns)
   static_assert(sizeof(FusedScratch<kSharedThreads>) <= sizeof(slot0), "merge scratch must fit a ring slot");
   static_assert(2 * sizeof(ChunkScratch) <= sizeof(slot0), "chunk merge scratch must fit a ring slot");
   static_assert(256 * MCH * 16 <= sizeof(slot0), "team merge round must fit a ring slot");
@@ -945,6 +1012,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
     rb0 = prefill_subtile(a, b / a.nkv, sub_rows);
     rb1 = sub_rows > 0 ? rb0 + 1 : rb0;
   }
+  int n_tiles = 0;  // wave-uniform count of s_tiles entries
   for (int t0 = rb0; t0 < rb1;) {
     const Tile tile = tile_rows(a, t0, lane, sub_rows);
     const int nrows = tile.nrows;
@@ -1245,28 +1313,25 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
     }
     __syncthreads();  // the team-merge area (slot 0) is free again
-    if (fused && !a.coop)
-      fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
-                                      reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
+    if (fused) {
+      if (a.spin_ticks > 0) {
+        // merged after the page loop (its registers are free then)
+        if (tid == 0) s_tiles[n_tiles] = int3{t0, nrows, ncols};
+        ++n_tiles;
+      } else {
+        fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
+                                        reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
+      }
+    }
     t0 += nrows;
     __syncthreads();  // LDS is reused by the next tile
   }
-  if (a.splits > 1 && a.counters != nullptr && a.coop) {
-    // every workgroup is resident: after one grid barrier all partials are
-    // complete, and each workgroup merges its share of the launch's outputs,
-    // two chunks of 32 elements at a time (one per 256-thread half)
-    grid_barrier(a.counters, static_cast<int>(gridDim.x));
-    ChunkScratch *cs = reinterpret_cast<ChunkScratch *>(slot0);
-    const int half = tid >> 8;
-    const int64_t per_row = HD / 32;
-    const int64_t nchunks = static_cast<int64_t>(a.rows) * a.nh * per_row;
-    for (int64_t c0 = 2 * static_cast<int64_t>(blockIdx.x); c0 < nchunks; c0 += 2 * static_cast<int64_t>(gridDim.x)) {
-      const int64_t c = c0 + half;
-      const bool live = c < nchunks;
-      const int64_t cc = live ? c : c0;
-      merge_chunk32(a, LoadCoherent{}, cc / per_row, static_cast<int>(cc % per_row) * 32, HD, tid & 255, live,
-                    cs[half]);
-    }
+  for (int i = 0; i < n_tiles; ++i) {
+    const int3 tl = s_tiles[i];
+    const int ncols_i = tl.z;
+    claimed_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, ncols_i, CAP, reinterpret_cast<ChunkScratch *>(slot0),
+                                      &s_is_last);
+    __syncthreads();
   }
 }
 
@@ -1311,8 +1376,6 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
   return p;
 }
 
-// Workgroups of pgqa_shared_kernel<HD, NSL> that the current device holds at
-// once (0 if it cannot launch cooperatively); computed once per device.
 // Prefill: tiles have many rows, so the shared-page kernel takes every hd
 // from 128 up with 64-column tiles (32 at hd 512), reading each page once per
 // 64 columns; hd 64 keeps the per-wave kernel's 16-column tiles.
@@ -1327,55 +1390,23 @@ Plan make_prefill_plan(int64_t group, int64_t hd) {
 }
 
 template <int HD, int NSL>
-int64_t coop_capacity() {
-  constexpr int kMaxDevices = 64;
-  static int64_t cap[kMaxDevices];
-  static bool known[kMaxDevices];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return 0;
-  if (!known[dev]) {
-    int coop = 0, cus = 0, per_cu = 0;
-    int64_t c = 0;
-    if (hipDeviceGetAttribute(&coop, hipDeviceAttributeCooperativeLaunch, dev) == hipSuccess && coop &&
-        hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, reinterpret_cast<const void *>(pgqa_shared_kernel<HD, NSL>),
-                                                     kSharedThreads, 0) == hipSuccess)
-      c = static_cast<int64_t>(cus) * per_cu;
-    cap[dev] = c;
-    known[dev] = true;
-  }
-  return cap[dev];
-}
-
-template <int HD, int NSL>
-hipError_t launch_shared(DecodeArgs a, int64_t blocks, bool want_coop, hipStream_t stream) {
-  const dim3 grid(static_cast<unsigned>(blocks)), block(kSharedThreads);
-  a.coop = want_coop && blocks <= coop_capacity<HD, NSL>();
-  if (a.coop) {
-    void *args[] = {&a};
-    if (hipLaunchCooperativeKernel(reinterpret_cast<const void *>(pgqa_shared_kernel<HD, NSL>), grid, block, args, 0,
-                                   stream) == hipSuccess)
-      return hipSuccess;
-    (void)hipGetLastError();  // refused (e.g. the device is shared): launch it the ordinary way
-    a.coop = 0;
-  }
-  hipLaunchKernelGGL((pgqa_shared_kernel<HD, NSL>), grid, block, 0, stream, a);
+hipError_t launch_shared(const DecodeArgs &a, int64_t blocks, hipStream_t stream) {
+  hipLaunchKernelGGL((pgqa_shared_kernel<HD, NSL>), dim3(static_cast<unsigned>(blocks)), dim3(kSharedThreads), 0,
+                     stream, a);
   return hipGetLastError();
 }
 
-// want_coop: a fused merge was asked for; the shared-page kernel then merges
-// cooperatively when its whole grid fits on the device at once.
 template <int HD>
-hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, bool want_coop, hipStream_t stream) {
+hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if constexpr (HD >= 128) {
     if (p.kind == 1) {
-      if (p.nsl == 2) return launch_shared<HD, 2>(a, blocks, want_coop, stream);
+      if (p.nsl == 2) return launch_shared<HD, 2>(a, blocks, stream);
       if constexpr (HD < 512) {
-        if (p.nsl == 1) return launch_shared<HD, 1>(a, blocks, want_coop, stream);
+        if (p.nsl == 1) return launch_shared<HD, 1>(a, blocks, stream);
       }
       if constexpr (HD >= 256) {
-        if (p.nsl == 4) return launch_shared<HD, 4>(a, blocks, want_coop, stream);
+        if (p.nsl == 4) return launch_shared<HD, 4>(a, blocks, stream);
       }
       return hipErrorInvalidValue;
     }
@@ -1489,19 +1520,19 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   // decides how the launch ends.
   a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
 
-  a.coop = 0;
-  // The last-workgroup merge of one unit reads splits * cap * hd floats.  From
-  // 2 MB up, one workgroup is too slow for that, and a cooperative launch
-  // (about 10 us more launch latency, then every workgroup merges a share)
-  // wins.
-  const bool want_coop = counters != nullptr && splits > 1 && splits * plan.cap * hd * 4 >= kCoopMergeBytes;
+  // The merge of one unit reads splits * cap * hd floats of partials: from
+  // 2 MB up the unit's workgroups merge it together (shared-page kernel),
+  // below that the last one to arrive merges it alone.
+  a.spin_ticks = counters != nullptr && splits > 1 && plan.kind == 1 && splits * plan.cap * hd * 4 >= kParallelMergeBytes
+                     ? kClaimSpinTicks
+                     : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   switch (hd) {
-    case 64: err = launch_decode<64>(a, plan, blocks, want_coop, st); break;
-    case 128: err = launch_decode<128>(a, plan, blocks, want_coop, st); break;
-    case 256: err = launch_decode<256>(a, plan, blocks, want_coop, st); break;
-    default: err = launch_decode<512>(a, plan, blocks, want_coop, st); break;
+    case 64: err = launch_decode<64>(a, plan, blocks, st); break;
+    case 128: err = launch_decode<128>(a, plan, blocks, st); break;
+    case 256: err = launch_decode<256>(a, plan, blocks, st); break;
+    default: err = launch_decode<512>(a, plan, blocks, st); break;
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {
@@ -1584,7 +1615,7 @@ int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *
   a.hblocks = plan.hblocks;
   a.cap = plan.cap;
   a.rank_rows = 0;
-  a.coop = 0;
+  a.spin_ticks = 0;
   a.tile_row0 = tile_row0;
   a.tile_nrows = tile_rows;
   a.ntiles = static_cast<int>(ntiles);
@@ -1593,10 +1624,10 @@ int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
   switch (hd) {
-    case 64: err = launch_decode<64>(a, plan, blocks, false, st); break;
-    case 128: err = launch_decode<128>(a, plan, blocks, false, st); break;
-    case 256: err = launch_decode<256>(a, plan, blocks, false, st); break;
-    default: err = launch_decode<512>(a, plan, blocks, false, st); break;
+    case 64: err = launch_decode<64>(a, plan, blocks, st); break;
+    case 128: err = launch_decode<128>(a, plan, blocks, st); break;
+    case 256: err = launch_decode<256>(a, plan, blocks, st); break;
+    default: err = launch_decode<512>(a, plan, blocks, st); break;
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "prefill kernel launch: %s", hipGetErrorString(err));
   return PGQA_OK;
