@@ -884,7 +884,7 @@ __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int n
     if (!ready) {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
       while (!ready && __builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(a.spin_ticks)) {
-        __builtin_amdgcn_s_sleep(2);
+        __builtin_amdgcn_s_sleep(20);  // ~1300 clocks: a few hundred waiters poll one word
         const int low = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
         if (low <= t) break;
         ready = low >= S;
@@ -897,11 +897,16 @@ __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int n
   for (;;) {
     __syncthreads();  // everyone has read the previous claim
     if (tid == 0) {
-      const int low = __hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
-      int slice = low - S;
-      if (slice < 0 || slice >= nslices) {
-        __hip_atomic_fetch_sub(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        slice = -1;
+      // look first: once every slice is claimed (or the word is reset) no
+      // atomic is needed to learn it
+      const int seen = (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff) - S;
+      int slice = -1;
+      if (seen >= 0 && seen < nslices) {
+        slice = (__hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff) - S;
+        if (slice < 0 || slice >= nslices) {
+          __hip_atomic_fetch_sub(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          slice = -1;
+        }
       }
       *s_word = slice;
     }
