@@ -1,34 +1,36 @@
-// Paged grouped-query decode attention for CDNA4 (gfx950): kernels + C ABI.
+// Paged grouped-query decode (and prefill) attention for CDNA4 (gfx950):
+// kernels + C ABI.
 //
 // What is computed is fixed by the span-02 GPU kernel test page
 // (respanai/span-02, engine/crates/kernels/tests/gpu.rs): its `reference`
 // function (scale 1.0, kv head h / (nh / nkv), causal with an optional sliding
-// window, pool [page][nkv][16][hd]) and its `attn_decode` calls (block table
-// with per-row origins, split partials merged by the last workgroup through a
-// counter or by a separate combine kernel, optional page map whose
-// out-of-window pages may point at a NaN-filled null page).  The page shows no
-// kernel code; everything below is designed for MI355X.
+// window, pool [page][nkv][16][hd]) and its `attn_decode` / `attn_prefill`
+// calls (block table with per-row origins, split partials merged by the last
+// workgroup through a counter or by a separate combine kernel, optional page
+// map whose out-of-window pages may point at a NaN-filled null page).  The
+// page shows no kernel code; everything below is designed for MI355X.
 //
 // Work decomposition
-//   * A "tile" is a run of up to `rmax` consecutive rows that share a page
-//     origin (rows of one sequence).  Its query heads for one kv head form up to
-//     16 "columns" (row, head), so one tile reads each KV page once for all of
-//     them.  Groups wider than 16 heads are cut into head blocks of 16.
-//   * A workgroup (4 waves) owns one (tile, kv head, head block, split).  The
-//     split is a contiguous range of the tile's visible pages; the 4 waves take
-//     its pages round robin and each keeps its own online-softmax state.
-//   * Per page and wave: K (16 tokens x hd) is loaded straight into MFMA
-//     operand registers and S^T = K Q^T is formed with
-//     v_mfma_f32_16x16x32_bf16 (tokens x columns).  The softmax weights come out
-//     laid out as the A operand of v_mfma_f32_16x16x16_bf16, so P V needs no
-//     shuffle of P; V is staged through LDS to read it token-major.  A column
-//     of ones appended to V yields the softmax denominators from the same MFMA.
-//   * The 4 wave states are merged through LDS (fixed tree), then the
-//     workgroup either writes the normalised bf16 output (1 split) or an f32
-//     partial (o, m, l).  Partials are merged, in split order 0..S-1, by one
-//     device routine used both by the last workgroup of a merge unit (fused,
-//     counter ticket) and by the separate combine kernel, so the two paths give
-//     the same bits.
+//   * A "tile" is a run of consecutive rows that share a page origin (rows of
+//     one sequence).  Its query heads for one kv head form "columns" (row,
+//     head); one tile reads each KV page once for all of its columns.  Groups
+//     wider than a tile are cut into head blocks.
+//   * Scores are S^T = K Q^T on v_mfma_f32_16x16x32_bf16 (16 tokens x 16
+//     columns); the softmax weights come out laid out as the A operand of
+//     v_mfma_f32_16x16x16_bf16, so P V needs no shuffle of P; V reaches the B
+//     operand through the LDS transpose read; a column of ones appended to V
+//     yields the softmax denominators from the same MFMA.
+//   * pgqa_wave_kernel: 16-column tiles, 4 waves each taking every 4th page of
+//     the split with their own softmax state (K straight from HBM into MFMA
+//     operand registers); narrow groups, batched decode.
+//   * pgqa_shared_kernel: up to 64-column tiles, 8 waves in two teams taking
+//     alternating pages staged in LDS by direct-to-LDS loads; groups of 8+
+//     with several rows, every hd-512 call, prefill.
+//   * With S splits, each (tile, kv head, head block, split) workgroup writes
+//     an f32 partial (o, m, l); the merge (fixed order: 8 interleaved groups of
+//     splits, each an fma chain) runs in the last workgroup of the unit, in
+//     all of the unit's workgroups together (large merges), or in the separate
+//     combine kernel -- the same arithmetic per element, so the same bits.
 //   * Masked scores are replaced by -inf with a select and V rows of tokens no
 //     column can see are zeroed with a select, so a NaN page or NaN slot outside
 //     every window cannot leak into the result.
