@@ -54,11 +54,13 @@ class DeviceWorkload:
         w = self.w
         if tiles is None:
             tiles = pg.make_tiles(w.page_origin, pg.prefill_rows_per_tile(w.hd))
-        t0, tn = dev_i32(tiles[0]), dev_i32(tiles[1])
+        t0, tn = tiles
+        if not isinstance(t0, torch.Tensor):  # host arrays: upload
+            t0, tn = dev_i32(t0), dev_i32(tn)
         if out is None:
             out = torch.empty((w.rows, w.nh, w.hd), dtype=torch.int16, device="cuda")
         pg.attn_prefill(out, self.q, self.k, self.v, self.bt, self.off, self.qpos, self.last, t0, tn,
-                        len(tiles[0]), w.rows, w.nh, w.nkv, w.hd, w.window, self.pmap)
+                        len(t0), w.rows, w.nh, w.nkv, w.hd, w.window, self.pmap)
         if sync:
             torch.cuda.synchronize()
         return out
