@@ -36,3 +36,24 @@ def attend(q_row, k_seq, v_seq, qpos, last, window):
         ex[p] = mpmath.exp(s)
     z = mpmath.fsum(ex.values())
     return [mpmath.fsum(ex[p] * _bf16(v_seq[p][d]) for p in vis) / z for d in range(hd)]
+
+
+def prep_head(x_bits, w_bits, cos_row, sin_row, rotary_dim, eps, rotate=True):
+    """QK-norm + RoPE of one head in 50-digit arithmetic (a pin for the prep
+    oracle).  The norm divides by the root of the mean square (plus eps); the
+    weight (None = 1) scales each element; the first ``rotary_dim`` elements
+    are rotated as complex numbers ``z_i = n_i + j n_{i + rotary_dim / 2}``
+    multiplied by ``cos_i + j sin_i``.  Returns hd mpf values."""
+    hd = len(x_bits)
+    x = [_bf16(b) for b in x_bits]
+    ms = mpmath.fsum(v * v for v in x) / hd
+    r = 1 / mpmath.sqrt(ms + mpmath.mpf(eps))
+    w = [mpmath.mpf(1)] * hd if w_bits is None else [_bf16(b) for b in w_bits]
+    n = [x[d] * r * w[d] for d in range(hd)]
+    y = list(n)
+    if rotate and rotary_dim:
+        h = rotary_dim // 2
+        for i in range(h):
+            z = mpmath.mpc(n[i], n[i + h]) * mpmath.mpc(mpmath.mpf(float(cos_row[i])), mpmath.mpf(float(sin_row[i])))
+            y[i], y[i + h] = z.real, z.imag
+    return y

@@ -269,3 +269,181 @@ NAMES = ("C1", "C2", "C3", "C4", "C4nan", "C5w0", "C5w4096", "PA", "PB")
 def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
     """Widen bf16 bit patterns to float32 (exact)."""
     return (b.astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+# ---------------------------------------------------------------------------
+# Inputs of the QK-norm + RoPE prep (the step that fills the pool before
+# decode; pegainfer pull request page #1002).  Per token: raw query, key and
+# value heads, the norm weights and the rotary tables, a position, and the
+# page addressing of the decode workloads above.
+# ---------------------------------------------------------------------------
+
+def _bf16_trunc(x: np.ndarray) -> np.ndarray:
+    return (np.asarray(x, dtype=np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def rope_tables(positions: int, rotary_dim: int, base: float = 10000.0):
+    """Rotary tables ``cos[p][i], sin[p][i]`` of the angle ``p * base^(-2i /
+    rotary_dim)`` for ``i < rotary_dim / 2``: computed in f64, stored as f32
+    (the prep takes the tables as inputs, as the page's fixtures build them)."""
+    half = rotary_dim // 2
+    if half == 0:
+        return np.zeros((max(positions, 1), 1), np.float32), np.zeros((max(positions, 1), 1), np.float32)
+    inv = base ** (-2.0 * np.arange(half, dtype=np.float64) / rotary_dim)
+    ang = np.arange(positions, dtype=np.float64)[:, None] * inv[None, :]
+    return np.cos(ang).astype(np.float32), np.sin(ang).astype(np.float32)
+
+
+@dataclasses.dataclass
+class PrepWorkload:
+    """One prep call's inputs (host numpy; bf16 as uint16 bits).  ``v_in``
+    None is the K = V form; ``q_w`` / ``k_w`` None mean weight 1."""
+
+    name: str
+    nh: int
+    nkv: int
+    hd: int
+    rotary_dim: int
+    eps: float
+    q_in: np.ndarray  # uint16 [tokens, nh, hd]
+    k_in: np.ndarray  # uint16 [tokens, nkv, hd]
+    v_in: Optional[np.ndarray]  # uint16 [tokens, nkv, hd] or None
+    q_w: Optional[np.ndarray]  # uint16 [hd]
+    k_w: Optional[np.ndarray]  # uint16 [hd]
+    rope_cos: np.ndarray  # f32 [positions, max(rotary_dim / 2, 1)]
+    rope_sin: np.ndarray
+    pos: np.ndarray  # int32 [tokens]
+    block_table: np.ndarray  # int32
+    page_origin: np.ndarray  # int32 [tokens]
+    npages: int
+    page_map: Optional[np.ndarray] = None
+    note: str = ""
+
+    @property
+    def tokens(self) -> int:
+        return int(self.pos.shape[0])
+
+    def zero_pools(self):
+        shape = (self.npages, self.nkv, PAGE, self.hd)
+        return np.zeros(shape, np.uint16), np.zeros(shape, np.uint16)
+
+    def replace(self, **kw) -> "PrepWorkload":
+        return dataclasses.replace(self, **kw)
+
+
+def _prep_data(rng: Lcg, tokens: int, nh: int, nkv: int, hd: int, kv_equal: bool, weights: bool):
+    q = rng.uniform_bf16(tokens * nh * hd).reshape(tokens, nh, hd)
+    k = rng.uniform_bf16(tokens * nkv * hd).reshape(tokens, nkv, hd)
+    v = None if kv_equal else rng.uniform_bf16(tokens * nkv * hd).reshape(tokens, nkv, hd)
+    qw = kw = None
+    if weights:  # 1 + x / 2, x uniform in [-1, 1): weights in [0.5, 1.5)
+        qw = _bf16_trunc(1.0 + 0.5 * bf16_bits_to_f32(rng.uniform_bf16(hd)))
+        kw = _bf16_trunc(1.0 + 0.5 * bf16_bits_to_f32(rng.uniform_bf16(hd)))
+    return q, k, v, qw, kw
+
+
+def prep_prefill(name: str, tokens: int, nh: int, nkv: int, hd: int, rotary_dim: int, p0: int = 0,
+                 kv_equal: bool = False, weights: bool = True, eps: float = 1e-6, base: float = 10000.0,
+                 seed: Optional[int] = None, shuffle: bool = True) -> PrepWorkload:
+    """Prefill form: positions ``p0 .. p0 + tokens - 1`` of one sequence, every
+    token at origin 0 of a table of ``ceil((p0 + tokens) / 16)`` entries.  The
+    sequence's pages are physical pages ``1..P``, shuffled (Fisher-Yates on
+    ``Lcg(seed + 1)``) unless ``shuffle`` is False; physical page 0 is never
+    in the table (a sentinel that must stay untouched).  Data from
+    ``Lcg(seed)``, seed ``24680 + hd`` by default."""
+    seed = 24680 + hd if seed is None else seed
+    npg = (p0 + tokens + PAGE - 1) // PAGE
+    perm = list(range(1, npg + 1))
+    if shuffle:
+        r = Lcg(seed + 1)
+        for i in range(npg - 1, 0, -1):
+            j = r.u32() % (i + 1)
+            perm[i], perm[j] = perm[j], perm[i]
+    q, k, v, qw, kw = _prep_data(Lcg(seed), tokens, nh, nkv, hd, kv_equal, weights)
+    pos = np.arange(p0, p0 + tokens, dtype=np.int32)
+    cos_t, sin_t = rope_tables(p0 + tokens, rotary_dim, base)
+    return PrepWorkload(name, nh, nkv, hd, rotary_dim, eps, q, k, v, qw, kw, cos_t, sin_t, pos,
+                        np.array(perm, np.int32), np.zeros(tokens, np.int32), npg + 1,
+                        note=f"prefill positions {p0}..{p0 + tokens - 1}")
+
+
+def prep_decode(name: str, nseq: int, lmin: int, lmax: int, nh: int, nkv: int, hd: int, rotary_dim: int,
+                kv_equal: bool = False, weights: bool = True, eps: float = 1e-6, base: float = 10000.0,
+                len_seed: int = 777, seed: Optional[int] = None, pad: int = 16) -> PrepWorkload:
+    """Batched decode form: one new token per sequence, at position ``L_s - 1``
+    of a sequence of length ``L_s`` (lengths and the page shuffle drawn as in
+    ``batched``), so every token has its own distinct, non-zero origin into
+    one concatenated table whose first ``pad`` entries point at physical page
+    0 (a sentinel that must stay untouched)."""
+    seed = 24680 + hd if seed is None else seed
+    r = Lcg(len_seed)
+    lens = [lmin + r.u32() % (lmax - lmin + 1) for _ in range(nseq)]
+    pages = [(L + PAGE - 1) // PAGE for L in lens]
+    total = sum(pages)
+    perm = list(range(1, total + 1))
+    for i in range(total - 1, 0, -1):
+        j = r.u32() % (i + 1)
+        perm[i], perm[j] = perm[j], perm[i]
+    bt = np.array([0] * pad + perm, dtype=np.int32)
+    origins = (np.cumsum([0] + pages[:-1]) + pad).astype(np.int32)
+    q, k, v, qw, kw = _prep_data(Lcg(seed), nseq, nh, nkv, hd, kv_equal, weights)
+    pos = np.array([L - 1 for L in lens], dtype=np.int32)
+    cos_t, sin_t = rope_tables(int(pos.max()) + 1, rotary_dim, base)
+    return PrepWorkload(name, nh, nkv, hd, rotary_dim, eps, q, k, v, qw, kw, cos_t, sin_t, pos, bt,
+                        origins, total + 1, note=f"{nseq} seqs, lengths U[{lmin},{lmax}] seed {len_seed}")
+
+
+def compress_windows(w: PrepWorkload, pad: Optional[int] = None) -> PrepWorkload:
+    """The same tokens, each behind its own table window that starts at the
+    token's own page -- what a caller that released the front of a sequence
+    passes.  Token t's window (the rest of its table from entry
+    ``origin_t + pos_t // 16``) is copied to its own place in a new table after
+    ``pad`` entries that point at physical page 0; its origin becomes
+    ``place_t - pos_t // 16`` (distinct, non-zero).  Every token's slot resolves
+    to the same physical page as before."""
+    first = [int(w.page_origin[t]) + int(w.pos[t]) // PAGE for t in range(w.tokens)]
+    pad = max(int(w.pos.max()) // PAGE + 1, 1) if pad is None else pad
+    parts = [np.zeros(pad, np.int32)]
+    origins = np.empty(w.tokens, np.int32)
+    place = pad
+    for t in range(w.tokens):
+        span = w.block_table[first[t]:first[t] + 2]  # the token's page and the next
+        origins[t] = place - int(w.pos[t]) // PAGE
+        parts.append(np.asarray(span, np.int32))
+        place += len(span)
+    return w.replace(name=w.name + "+compressed", block_table=np.concatenate(parts),
+                     page_origin=origins, note=w.note + ", per-token compressed windows")
+
+
+def prep_with_page_map(w: PrepWorkload) -> PrepWorkload:
+    """Every table entry ``e`` goes through a page map: the table is replaced
+    by ``0..len-1`` (identity entries) and ``page_map[e]`` is the physical page
+    the entry held; page 0 stays the untouched sentinel."""
+    return w.replace(name=w.name + "+pagemap", page_map=np.asarray(w.block_table, np.int32).copy(),
+                     block_table=np.arange(len(w.block_table), dtype=np.int32),
+                     note=w.note + ", through a page map")
+
+
+def make_prep(name: str) -> PrepWorkload:
+    """Named prep shapes: hd 256 with full and partial rotation, hd 512 with
+    V = K and rotary_dim 128 (the two gate families on the page), and the
+    decode shapes' hd 128 / 64 with the batched decode form."""
+    n = name.upper()
+    if n == "R256F":
+        return prep_prefill("R256F", tokens=48, nh=16, nkv=8, hd=256, rotary_dim=256, p0=5)
+    if n == "R256P":
+        return prep_prefill("R256P", tokens=40, nh=16, nkv=8, hd=256, rotary_dim=128, p0=21)
+    if n == "R512KV":
+        return prep_prefill("R512KV", tokens=36, nh=16, nkv=2, hd=512, rotary_dim=128, p0=3, kv_equal=True,
+                            base=1000000.0)
+    if n == "R128D":
+        return prep_decode("R128D", nseq=64, lmin=17, lmax=2000, nh=32, nkv=8, hd=128, rotary_dim=128)
+    if n == "R64D":
+        return prep_decode("R64D", nseq=9, lmin=1, lmax=300, nh=4, nkv=1, hd=64, rotary_dim=32,
+                           weights=False)
+    if n == "R128P8K":
+        return prep_prefill("R128P8K", tokens=8192, nh=32, nkv=8, hd=128, rotary_dim=128)
+    raise KeyError(name)
+
+
+PREP_NAMES = ("R256F", "R256P", "R512KV", "R128D", "R64D")
