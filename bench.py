@@ -65,9 +65,9 @@ def kv_bytes(w) -> int:
     return visible_union_tokens(w) * w.nkv * w.hd * 2 * 2
 
 
-def kernel_source_hash() -> str:
+def kernel_source_hash(source: str = "pgqa.hip") -> str:
     h = hashlib.sha256()
-    with open(os.path.join(ROOT, "paged_gqa_decode_attn_amd", "csrc", "pgqa.hip"), "rb") as f:
+    with open(os.path.join(ROOT, "paged_gqa_decode_attn_amd", "csrc", source), "rb") as f:
         h.update(f.read())
     return h.hexdigest()[:16]
 
@@ -81,7 +81,7 @@ def committed_traffic(config: str):
             rec = json.load(f).get(config)
     except (OSError, ValueError):
         return None
-    if not rec or rec.get("kernel_sha") != kernel_source_hash():
+    if not rec or rec.get("kernel_sha") != kernel_source_hash(rec.get("kernel_source", "pgqa.hip")):
         return None
     return rec.get("bytes_per_launch")
 
@@ -186,6 +186,49 @@ def run_prefill(w, steps, warmup, flush):
             "tiles": len(t0)}
 
 
+def prep_bytes(w) -> int:
+    """Algorithmic bytes of a QK-norm + RoPE prep: every input head read once
+    and every output head written once (bf16), each token's rotary-table row
+    (cos and sin, f32) and metadata (position, origin, table entry) read once,
+    the two norm weights once."""
+    heads = w.nh + 2 * w.nkv
+    per_token = heads * w.hd * 2 * 2 + w.rotary_dim * 4 + 3 * 4
+    return w.tokens * per_token + 2 * w.hd * 2
+
+
+def run_prep(w, steps, warmup, flush):
+    """Time pgqa_qk_rope_prep over every token of w into resident pools."""
+    import torch
+
+    from tests.gpu_util import DevicePrep  # upload helper only
+
+    d = DevicePrep(w)
+    shape = (w.npages, w.nkv, 16, w.hd)
+    kp = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    vp = torch.zeros(shape, dtype=torch.int16, device="cuda")
+    qo = torch.empty((w.tokens, w.nh, w.hd), dtype=torch.int16, device="cuda")
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda") if flush else None
+    sink = torch.zeros((), dtype=torch.float32, device="cuda") if flush else None
+    for _ in range(warmup):
+        d.run(kp, vp, qo, sync=False)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    for i in range(steps):
+        if scratch is not None:
+            torch.sum(scratch, dim=0, out=sink)  # reads 1 GiB, writes 4 bytes
+        ev[i][0].record(stream)
+        d.run(kp, vp, qo, sync=False)
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+    b = prep_bytes(w)
+    gbs = b / (ms * 1e-3) / 1e9
+    return {"tokens": w.tokens, "us_per_call": round(ms * 1e3, 2), "GB/s": round(gbs, 1),
+            "frac": round(gbs / HBM_PEAK_GBS, 4), "bytes": b, "traffic": committed_traffic(w.name),
+            "nh": w.nh, "nkv": w.nkv, "hd": w.hd, "rotary_dim": w.rotary_dim}
+
+
 def cpu_baseline(w, budget_s=12.0):
     """The oracle, as it stands, on a bounded sample of the workload: the first
     n rows, n growing by 4x until a call costs a quarter of the budget; a sample
@@ -233,6 +276,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
+    ap.add_argument("--prep", default="",
+                    help="only time the QK-norm + RoPE prep on this prep workload (e.g. R128P8K); one JSON line")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU only: the decode path here runs on a single GPU "
@@ -249,6 +294,10 @@ def main():
             dst.copy_(src)
         torch.cuda.synchronize()
         log("[bench] copied 1 GiB 5 times")
+        return
+    if args.prep:
+        r = run_prep(workloads.make_prep(args.prep), args.steps, args.warmup, not args.no_flush)
+        print(json.dumps({"prep": args.prep, **r}), flush=True)
         return
     res = run_config(args.config, args.steps, args.warmup, args.mode, args.splits, not args.no_flush)
     w = res.pop("_w")
@@ -293,6 +342,11 @@ def main():
                           ("prefill_8k", workloads.single_sequence("pf8k", ctx=8192, rows=8192, nh=16, nkv=8,
                                                                    hd=256, window=0))):
             secondary[pname] = run_prefill(pw, 10, 2, not args.no_flush)
+            torch.cuda.empty_cache()
+        # QK-norm + RoPE prep into the pool (HBM-bound): an 8K-token prefill
+        # and a 64-sequence decode step of the batched decode's head layout
+        for pname, wname in (("prep_prefill_8k", "R128P8K"), ("prep_decode_64", "R128D")):
+            secondary[pname] = run_prep(workloads.make_prep(wname), 20, 3, not args.no_flush)
             torch.cuda.empty_cache()
 
     ms = res["kernel_ms_mean"]

@@ -185,6 +185,46 @@ int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *
                       const int32_t *tile_row0, const int32_t *tile_rows, int64_t ntiles, int64_t rows, int64_t nh,
                       int64_t nkv, int64_t hd, int64_t window, const int32_t *page_map, void *stream);
 
+/*
+ * QK-norm + RoPE prep: the step before decode that fills the paged pool
+ * (pegainfer pull request page #1002, the HD256/HD512 QK-RoPE gates: RMSNorm
+ * of the query and key heads with norm weights, rotary embedding from
+ * position tables over the first rotary_dim elements as a low and a high
+ * half with a pass-through tail, a weightless norm for V, V from the K input
+ * in the hd-512 "K = V" form, the results landing at the paged layout's
+ * addresses through per-token page origins).  The page prints no formulas;
+ * the reading taken, per token t and head:
+ *   n_d = x_d * w_d / sqrt(sum_d(x_d^2) / hd + eps)   (w_d = 1: V, or no weight)
+ *   for i < rotary_dim / 2, h = rotary_dim / 2, c = cos[pos_t][i], s = sin[pos_t][i]:
+ *     y_i = n_i c - n_{i+h} s,   y_{i+h} = n_{i+h} c + n_i s
+ *   y_d = n_d for d >= rotary_dim; V heads are never rotated.
+ * Computed in f32, stored as bf16 rounded to nearest even.
+ *   q_out        bf16 [tokens][nh][hd]: the rotated query heads.  May be q_in
+ *                itself (in place); must not overlap anything else.
+ *   k_pool, v_pool  bf16 [npages][nkv][16][hd]: kv head kh of token t is
+ *                written at page phys = block_table[page_origin[t] + pos[t] / 16]
+ *                (then page_map[phys] when page_map is not NULL), slot
+ *                pos[t] % 16 -- the addressing pgqa_attn_decode reads.  Nothing
+ *                else in the pools is touched.  Two tokens with the same slot
+ *                race.
+ *   q_in         bf16 [tokens][nh][hd];  k_in bf16 [tokens][nkv][hd]
+ *   v_in         bf16 [tokens][nkv][hd], or NULL: V is normalised from k_in
+ *   q_weight, k_weight  bf16 [hd] norm weights, or NULL for weight 1
+ *   rope_cos, rope_sin  f32 [positions][rotary_dim / 2] (row pos[t] is read);
+ *                may be NULL when rotary_dim is 0
+ *   pos          int32 [tokens], >= 0 (and < the tables' rows when rotating)
+ *   block_table, page_origin (int32 [tokens]), page_map: as for decode; the
+ *                caller guarantees every reached entry and page is valid
+ *   rotary_dim   a multiple of 16 in 0 .. hd;  eps finite, >= 0
+ * Every bf16 buffer and both tables must be 16-byte aligned.  tokens == 0
+ * enqueues nothing.  Returns PGQA_OK, PGQA_EINVAL or PGQA_ELAUNCH.
+ */
+int pgqa_qk_rope_prep(void *q_out, void *k_pool, void *v_pool, const void *q_in, const void *k_in, const void *v_in,
+                      const void *q_weight, const void *k_weight, const float *rope_cos, const float *rope_sin,
+                      const int32_t *pos, const int32_t *block_table, const int32_t *page_origin,
+                      const int32_t *page_map, int64_t tokens, int64_t nh, int64_t nkv, int64_t hd,
+                      int64_t rotary_dim, float eps, void *stream);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pgqa_last_error(void);
 

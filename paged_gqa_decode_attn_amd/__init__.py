@@ -9,7 +9,8 @@ CPU or framework fallback, and a missing library is an error.
 Entry points (same names and argument order as the C ABI, after the span-02
 GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
 ``counter_capacity``, ``attn_decode``, ``prefill_rows_per_tile``,
-``make_tiles``, ``attn_prefill``.
+``make_tiles``, ``attn_prefill``; and ``qk_rope_prep``, the QK-norm + RoPE
+step that fills the pool before decode.
 """
 from __future__ import annotations
 
@@ -59,6 +60,8 @@ def lib() -> ctypes.CDLL:
         h.pgqa_make_tiles.argtypes = [p, i64, i64, p, p, i64]
         h.pgqa_attn_prefill.restype = ctypes.c_int
         h.pgqa_attn_prefill.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
+        h.pgqa_qk_rope_prep.restype = ctypes.c_int
+        h.pgqa_qk_rope_prep.argtypes = [p] * 14 + [i64, i64, i64, i64, i64, ctypes.c_float, p]
         _lib = h
     return _lib
 
@@ -187,5 +190,47 @@ def attn_prefill(out, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     rc = lib().pgqa_attn_prefill(*args, ntiles, rows, nh, nkv, hd, window, pm, stream)
+    if rc != OK:
+        raise PgqaError(rc, last_error())
+
+
+def qk_rope_prep(q_out, k_pool, v_pool, q_in, k_in, v_in, q_weight, k_weight, rope_cos, rope_sin, pos,
+                 block_table, page_origin, tokens: int, nh: int, nkv: int, hd: int, rotary_dim: int,
+                 eps: float, page_map=None, stream=None) -> None:
+    """Enqueue one QK-norm + RoPE prep (see ``pgqa_qk_rope_prep`` in include/pgqa.h).
+
+    bf16 (or 16-bit integer views) ``q_out`` / ``q_in`` [tokens][nh][hd],
+    ``k_in`` / ``v_in`` [tokens][nkv][hd] (``v_in`` None: V from ``k_in``),
+    pools [npages][nkv][16][hd], weights [hd] or None; f32 rotary tables
+    [positions][rotary_dim / 2] (None when rotary_dim is 0); int32 ``pos``,
+    ``block_table``, ``page_origin``, ``page_map``."""
+    import torch
+
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    i32 = (torch.int32,)
+    f32 = (torch.float32,)
+    nq = tokens * nh * hd
+    nk = tokens * nkv * hd
+    args = [
+        _addr(q_out, "q_out", b16, nq),
+        _addr(k_pool, "k_pool", b16),
+        _addr(v_pool, "v_pool", b16),
+        _addr(q_in, "q_in", b16, nq),
+        _addr(k_in, "k_in", b16, nk),
+        _addr(v_in, "v_in", b16, nk),
+        _addr(q_weight, "q_weight", b16, hd),
+        _addr(k_weight, "k_weight", b16, hd),
+        _addr(rope_cos, "rope_cos", f32),
+        _addr(rope_sin, "rope_sin", f32),
+        _addr(pos, "pos", i32, tokens),
+        _addr(block_table, "block_table", i32),
+        _addr(page_origin, "page_origin", i32, tokens),
+        _addr(page_map, "page_map", i32),
+    ]
+    if stream is None:
+        stream = torch.cuda.current_stream(q_out.device if hasattr(q_out, "device") else None).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = lib().pgqa_qk_rope_prep(*args, tokens, nh, nkv, hd, rotary_dim, float(eps), stream)
     if rc != OK:
         raise PgqaError(rc, last_error())

@@ -4,7 +4,8 @@ import subprocess
 
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
-SRC = os.path.join(PKG, "csrc", "pgqa.hip")
+# decode / prefill attention, and the QK-norm + RoPE prep
+SRCS = [os.path.join(PKG, "csrc", "pgqa.hip"), os.path.join(PKG, "csrc", "prep.hip")]
 LIB = os.path.join(PKG, "libpgqa.so")
 INCLUDE = os.path.join(ROOT, "include")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -22,7 +23,7 @@ FLAGS = [
 
 def build(extra=(), out=LIB, verbose=False):
     tmp = out + ".tmp%d" % os.getpid()
-    cmd = [HIPCC] + FLAGS + list(extra) + ["-I", INCLUDE, SRC, "-o", tmp]
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-I", INCLUDE] + SRCS + ["-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in r.stderr.splitlines()
                     if "packed-fp32-ops' is not a recognized feature" not in l)

@@ -45,7 +45,26 @@
 #include <type_traits>
 #include <utility>
 
+#include "errors.h"
 #include "pgqa.h"
+
+namespace pgqa_detail {
+namespace {
+thread_local char g_error[512] = "";
+}  // namespace
+
+int fail(int code, const char *fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_error, sizeof g_error, fmt, ap);
+  va_end(ap);
+  return code;
+}
+
+void clear_error() { g_error[0] = '\0'; }
+
+const char *error_text() { return g_error; }
+}  // namespace pgqa_detail
 
 namespace {
 
@@ -1343,16 +1362,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
 }
 
 
-thread_local char g_error[512] = "";
-
-int fail(int code, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-int fail(int code, const char *fmt, ...) {
-  va_list ap;
-  va_start(ap, fmt);
-  vsnprintf(g_error, sizeof g_error, fmt, ap);
-  va_end(ap);
-  return code;
-}
+using pgqa_detail::fail;
 
 // Which kernel runs and how rows are tiled, from the call's shapes only (so
 // calls that differ only in data -- merge mode, page placement -- run the same
@@ -1458,14 +1468,14 @@ uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_
 
 int32_t pgqa_counter_capacity(void) { return kCounterCap; }
 
-const char *pgqa_last_error(void) { return g_error; }
+const char *pgqa_last_error(void) { return pgqa_detail::error_text(); }
 
 int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,
                      const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
                      const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
                      int64_t window, int64_t splits, int32_t *counters, const int32_t *page_map,
                      void *stream) {
-  g_error[0] = '\0';
+  pgqa_detail::clear_error();
   if (!out || !q || !k_pool || !v_pool || !block_table || !page_origin || !qpos || !kv_last)
     return fail(PGQA_EINVAL, "a required pointer is NULL");
   if (rows < 1 || rows > INT_MAX / 2) return fail(PGQA_EINVAL, "rows=%lld out of range", (long long)rows);
@@ -1557,7 +1567,7 @@ int32_t pgqa_prefill_rows_per_tile(int64_t hd) {
 
 int64_t pgqa_make_tiles(const int32_t *page_origin, int64_t rows, int64_t rows_per_tile, int32_t *tile_row0,
                         int32_t *tile_rows, int64_t capacity) {
-  g_error[0] = '\0';
+  pgqa_detail::clear_error();
   if (!page_origin || !tile_row0 || !tile_rows || rows < 0 || rows > INT_MAX || rows_per_tile < 1 ||
       rows_per_tile > kPrefillRowsPerTile)
     return fail(PGQA_EINVAL, "make_tiles: bad arguments");
@@ -1578,7 +1588,7 @@ int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *
                       const int32_t *page_origin, const int32_t *qpos, const int32_t *kv_last,
                       const int32_t *tile_row0, const int32_t *tile_rows, int64_t ntiles, int64_t rows, int64_t nh,
                       int64_t nkv, int64_t hd, int64_t window, const int32_t *page_map, void *stream) {
-  g_error[0] = '\0';
+  pgqa_detail::clear_error();
   if (!out || !q || !k_pool || !v_pool || !block_table || !page_origin || !qpos || !kv_last || !tile_row0 ||
       !tile_rows)
     return fail(PGQA_EINVAL, "a required pointer is NULL");

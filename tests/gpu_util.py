@@ -14,6 +14,42 @@ def dev_i32(a):
     return torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
 
 
+def dev_f32(a):
+    return torch.from_numpy(np.ascontiguousarray(a, dtype=np.float32)).cuda()
+
+
+class DevicePrep:
+    """A prep workload's inputs on the device; ``run`` makes one
+    pgqa_qk_rope_prep call into zeroed (or given) pools."""
+
+    def __init__(self, w):
+        self.w = w
+        self.q_in = dev_i16(w.q_in)
+        self.k_in = dev_i16(w.k_in)
+        self.v_in = None if w.v_in is None else dev_i16(w.v_in)
+        self.q_w = None if w.q_w is None else dev_i16(w.q_w)
+        self.k_w = None if w.k_w is None else dev_i16(w.k_w)
+        self.cos = dev_f32(w.rope_cos) if w.rotary_dim else None
+        self.sin = dev_f32(w.rope_sin) if w.rotary_dim else None
+        self.pos = dev_i32(w.pos)
+        self.bt = dev_i32(w.block_table)
+        self.off = dev_i32(w.page_origin)
+        self.pmap = None if w.page_map is None else dev_i32(w.page_map)
+
+    def run(self, k_pool=None, v_pool=None, q_out=None, sync=True):
+        w = self.w
+        shape = (w.npages, w.nkv, 16, w.hd)
+        kp = torch.zeros(shape, dtype=torch.int16, device="cuda") if k_pool is None else k_pool
+        vp = torch.zeros(shape, dtype=torch.int16, device="cuda") if v_pool is None else v_pool
+        qo = torch.empty((w.tokens, w.nh, w.hd), dtype=torch.int16, device="cuda") if q_out is None else q_out
+        pg.qk_rope_prep(qo, kp, vp, self.q_in, self.k_in, self.v_in, self.q_w, self.k_w, self.cos, self.sin,
+                        self.pos, self.bt, self.off, w.tokens, w.nh, w.nkv, w.hd, w.rotary_dim, w.eps,
+                        page_map=self.pmap)
+        if sync:
+            torch.cuda.synchronize()
+        return qo, kp, vp
+
+
 class DeviceWorkload:
     def __init__(self, w):
         self.w = w

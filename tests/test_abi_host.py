@@ -22,7 +22,8 @@ def declared_functions():
 def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
-            "pgqa_counter_capacity", "pgqa_last_error"} <= set(names)
+            "pgqa_counter_capacity", "pgqa_last_error", "pgqa_attn_prefill", "pgqa_make_tiles",
+            "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep"} <= set(names)
     h = ctypes.CDLL(pg.LIB_PATH)
     for n in names:
         assert getattr(h, n, None) is not None, n
@@ -172,3 +173,31 @@ def pcall(**kw):
 def test_prefill_refusals(kw):
     assert pcall(**kw) == pg.EINVAL
     assert pg.last_error() != ""
+
+
+def rcall(**kw):
+    a = dict(qo=FAKE, kp=FAKE, vp=FAKE, qi=FAKE, ki=FAKE, vi=None, qw=None, kw=None, cos=FAKE, sin=FAKE,
+             pos=FAKE, bt=FAKE, off=FAKE, pmap=None, tokens=1, nh=4, nkv=1, hd=64, rd=64, eps=1e-6)
+    a.update(kw)
+    return pg.lib().pgqa_qk_rope_prep(a["qo"], a["kp"], a["vp"], a["qi"], a["ki"], a["vi"], a["qw"], a["kw"],
+                                      a["cos"], a["sin"], a["pos"], a["bt"], a["off"], a["pmap"], a["tokens"],
+                                      a["nh"], a["nkv"], a["hd"], a["rd"], a["eps"], None)
+
+
+@pytest.mark.parametrize("kw", [
+    dict(qo=None), dict(kp=None), dict(vp=None), dict(qi=None), dict(ki=None), dict(pos=None),
+    dict(bt=None), dict(off=None), dict(cos=None), dict(sin=None), dict(tokens=-1), dict(nh=0),
+    dict(nkv=0), dict(hd=96), dict(hd=1024), dict(rd=8), dict(rd=80), dict(rd=-16),
+    dict(eps=-1.0), dict(eps=float("nan")), dict(eps=float("inf")), dict(qi=FAKE + 2),
+    dict(vi=FAKE + 8), dict(qw=FAKE + 2), dict(cos=FAKE + 4), dict(kp=FAKE + 2),
+])
+def test_prep_refusals(kw):
+    assert rcall(**kw) == pg.EINVAL
+    assert pg.last_error() != ""
+
+
+def test_prep_accepts_without_launch():
+    # no tokens: nothing to enqueue (no device needed); no rotation: no tables needed
+    assert rcall(tokens=0) == pg.OK
+    assert rcall(tokens=0, rd=0, cos=None, sin=None) == pg.OK
+    assert pg.last_error() == ""
