@@ -281,9 +281,13 @@ __device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane,
 }
 
 // Prefill: sub-tile p of the launch -> its first row and row count (0: none,
-// also for a caller tile that would reach outside rows 0 .. rows - 1).
+// also for a caller tile that would reach outside rows 0 .. rows - 1).  The
+// sub-tiles are taken last first: in a causal prefill the later rows of a
+// sequence see the most keys, so the longest work is dispatched first and
+// the launch ends on short pieces.
 constexpr int kPrefillRowsPerTile = 64;
 __device__ __forceinline__ int prefill_subtile(const DecodeArgs &a, int p, int &nrows) {
+  p = a.ntiles * a.nsub - 1 - p;
   const int i = p / a.nsub, j = p - i * a.nsub;
   const int r0 = a.tile_row0[i], n = a.tile_nrows[i];
   nrows = 0;
@@ -966,14 +970,18 @@ __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int n
 // complete; the same barrier tells that the slot refilled next is free.
 // ---------------------------------------------------------------------------
 constexpr int kSharedThreads = 512;
-template <int HD, int NSL>
+template <int HD, int NSL, bool WIDE>
 __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;              // QK^T MFMA steps over the whole hd
   constexpr int DJ = HD / 16;              // PV MFMA output blocks over the whole hd
   constexpr int KS = KJ / NSL;             // ... per slice
   constexpr int DS = DJ / NSL;
   constexpr int QBM = kWaves / NSL;        // column blocks per team
-  constexpr int CAP = 16 * QBM;            // columns per tile
+  constexpr int CAP = 16 * QBM;            // columns per team
+  // WIDE (prefill, one split): the teams take different column blocks of a
+  // tile twice as wide and both compute every page of a pair, so a page is
+  // read once per 2 CAP columns and there is no team merge.
+  constexpr int TCAP = WIDE ? 2 * CAP : CAP;  // columns per tile
   constexpr int PAGE_ELEMS = kPage * HD;   // bf16 elements of one K (or V) page
   constexpr int SLOT_ELEMS = 4 * PAGE_ELEMS;  // a page pair: team 0's K, V, then team 1's
   constexpr int NP = HD == 512 ? 2 : HD == 256 ? 4 : 6;  // ring slots (128, 128, 96 KB)
@@ -1019,6 +1027,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   const int lc = lane >> 4;
   const int cb = w4 / NSL;     // this wave's column block
   const int sl = w4 % NSL;     // ... and hd slice
+  const int cbt = cb + (WIDE ? team * QBM : 0);  // column block within the tile
   const int j0 = sl * KS;      // first QK step of the slice
   const int jj0 = sl * DS;     // first PV block of the slice
 
@@ -1044,10 +1053,10 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
     const int nrows = tile.nrows;
     int pbeg, pend;
     split_range(tile, split, a.splits, pbeg, pend);
-    const int ncols = a.group <= CAP ? nrows * a.group : min(CAP, a.group - hb * CAP);
-    const bool active = 16 * cb < ncols;  // this wave's column block exists (wave-uniform)
+    const int ncols = a.group <= TCAP ? nrows * a.group : min(TCAP, a.group - hb * TCAP);
+    const bool active = 16 * cbt < ncols;  // this wave's column block exists (wave-uniform)
 
-    const Column col = tile_column(16 * cb + ln, a.group, nrows, hb, CAP);
+    const Column col = tile_column(16 * cbt + ln, a.group, nrows, hb, TCAP);
     const int col_lo = __shfl(tile.lo_l, col.row);
     // shuffle with every lane active, then drop columns without a row
     const int col_hi_any = __shfl(tile.hi_l, col.row);
@@ -1122,17 +1131,10 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
     };
 
-    // One pair: wait for it, refill the slot of the pair before it, compute this
-    // team's page of it.
-    auto step = [&](int j, const uint16_t *buf, uint16_t *refill) __attribute__((always_inline)) {
-      // this wave's loads of pair j have landed once at most the loads of the
-      // pairs after it are outstanding; the barrier then makes the whole pair
-      // visible and tells that the slot of pair j - 1 is no longer read
-      __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0f70);
-      lds_barrier();
-      issue_pair(j + NP - 1, refill);
-
-      const int k = 2 * j + team;
+    // Page pk of pair j (in the pair's ring slot `buf`) for this wave's
+    // columns: scores, online softmax, P V.
+    auto page = [&](int j, int pk, const uint16_t *buf) __attribute__((always_inline)) {
+      const int k = 2 * j + pk;
       const int p = pbeg + k;
       const bool full = p >= tile.fp0 && p < tile.fp1;  // the same in every wave of the team
       uint32_t tokmask = 0;
@@ -1152,7 +1154,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
       const bool work = tokmask != 0;  // the same in every wave of the team
 
-      const uint16_t *kt = buf + team * 2 * PAGE_ELEMS;
+      const uint16_t *kt = buf + pk * 2 * PAGE_ELEMS;
       const uint16_t *vt = kt + PAGE_ELEMS;
       // lane (4m+q) of group lc reads token 4 lc + m, columns 4q..4q+3 of each block
       const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * 16 + 4 * (ln & 3) + jj0 * 256;
@@ -1242,6 +1244,23 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
     };
 
+    // One pair: wait for it, refill the slot of the pair before it, compute this
+    // team's page of it (WIDE: both pages, for this team's columns).
+    auto step = [&](int j, const uint16_t *buf, uint16_t *refill) __attribute__((always_inline)) {
+      // this wave's loads of pair j have landed once at most the loads of the
+      // pairs after it are outstanding; the barrier then makes the whole pair
+      // visible and tells that the slot of pair j - 1 is no longer read
+      __builtin_amdgcn_s_waitcnt((INFLIGHT & 15) | ((INFLIGHT >> 4) << 14) | 0x0f70);
+      lds_barrier();
+      issue_pair(j + NP - 1, refill);
+      if constexpr (WIDE) {
+        page(j, 0, buf);
+        page(j, 1, buf);
+      } else {
+        page(j, team, buf);
+      }
+    };
+
     if (npairs > 0) {
       fetch_window(0);
       [&]<int... I>(std::integer_sequence<int, I...>) {
@@ -1269,55 +1288,58 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
         lo[i] = lacc[i];
       }
     }
-    float sa[4] = {1.f, 1.f, 1.f, 1.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
-    f32x4 *xm = reinterpret_cast<f32x4 *>(&xscore[0][0]);  // [w4][lane] (m x4, l x4)
-    __syncthreads();
-    if (team == 1) {
-      xm[(w4 * 64 + lane) * 2] = f32x4{mo[0], mo[1], mo[2], mo[3]};
-      xm[(w4 * 64 + lane) * 2 + 1] = f32x4{lo[0], lo[1], lo[2], lo[3]};
-    }
-    __syncthreads();
-    if (team == 0) {
-      const f32x4 mb = xm[(w4 * 64 + lane) * 2];
-      const f32x4 lb = xm[(w4 * 64 + lane) * 2 + 1];
-  #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float mm = fmaxf(mo[i], mb[i]);
-        sa[i] = mm == -INFINITY ? 0.f : fast_exp2(mo[i] - mm);
-        sb[i] = mm == -INFINITY ? 0.f : fast_exp2(mb[i] - mm);
-        lo[i] = lo[i] * sa[i] + lb[i] * sb[i];
-        mo[i] = mm;
+    if constexpr (!WIDE) {
+      float sa[4] = {1.f, 1.f, 1.f, 1.f}, sb[4] = {0.f, 0.f, 0.f, 0.f};
+      f32x4 *xm = reinterpret_cast<f32x4 *>(&xscore[0][0]);  // [w4][lane] (m x4, l x4)
+      __syncthreads();
+      if (team == 1) {
+        xm[(w4 * 64 + lane) * 2] = f32x4{mo[0], mo[1], mo[2], mo[3]};
+        xm[(w4 * 64 + lane) * 2 + 1] = f32x4{lo[0], lo[1], lo[2], lo[3]};
       }
-    }
-    {
-      f32x4 *xo = reinterpret_cast<f32x4 *>(slot0);  // [w4][u][lane]
-  #pragma unroll
-      for (int u0 = 0; u0 < DS; u0 += MCH) {
-        __syncthreads();
-        if (team == 1) {
-  #pragma unroll
-          for (int u = 0; u < MCH; ++u) xo[(w4 * MCH + u) * 64 + lane] = oacc[u0 + u];
+      __syncthreads();
+      if (team == 0) {
+        const f32x4 mb = xm[(w4 * 64 + lane) * 2];
+        const f32x4 lb = xm[(w4 * 64 + lane) * 2 + 1];
+    #pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float mm = fmaxf(mo[i], mb[i]);
+          sa[i] = mm == -INFINITY ? 0.f : fast_exp2(mo[i] - mm);
+          sb[i] = mm == -INFINITY ? 0.f : fast_exp2(mb[i] - mm);
+          lo[i] = lo[i] * sa[i] + lb[i] * sb[i];
+          mo[i] = mm;
         }
-        __syncthreads();
-        if (team == 0) {
-  #pragma unroll
-          for (int u = 0; u < MCH; ++u) {
-            const f32x4 ob = xo[(w4 * MCH + u) * 64 + lane];
-  #pragma unroll
-            for (int i = 0; i < 4; ++i) oacc[u0 + u][i] = oacc[u0 + u][i] * sa[i] + ob[i] * sb[i];
+      }
+      {
+        f32x4 *xo = reinterpret_cast<f32x4 *>(slot0);  // [w4][u][lane]
+    #pragma unroll
+        for (int u0 = 0; u0 < DS; u0 += MCH) {
+          __syncthreads();
+          if (team == 1) {
+    #pragma unroll
+            for (int u = 0; u < MCH; ++u) xo[(w4 * MCH + u) * 64 + lane] = oacc[u0 + u];
+          }
+          __syncthreads();
+          if (team == 0) {
+    #pragma unroll
+            for (int u = 0; u < MCH; ++u) {
+              const f32x4 ob = xo[(w4 * MCH + u) * 64 + lane];
+    #pragma unroll
+              for (int i = 0; i < 4; ++i) oacc[u0 + u][i] = oacc[u0 + u][i] * sa[i] + ob[i] * sb[i];
+            }
           }
         }
       }
     }
 
-    // ---- results: team 0, this wave's hd slice of its column block ----
-    const bool fused = a.splits > 1 && a.counters != nullptr;
-    if (team == 0 && active) {
+    // ---- results: team 0 (WIDE: both teams), this wave's hd slice of its
+    // column block ----
+    const bool fused = !WIDE && a.splits > 1 && a.counters != nullptr;
+    if ((WIDE || team == 0) && active) {
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const int r = 16 * cb + 4 * lc + i;
+        const int r = 16 * cbt + 4 * lc + i;
         if (r >= ncols) continue;
-        const Column rc = tile_column(r, a.group, nrows, hb, CAP);
+        const Column rc = tile_column(r, a.group, nrows, hb, TCAP);
         const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
         if (a.splits == 1) {
           const float l = lo[i];
@@ -1339,19 +1361,22 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
     }
     __syncthreads();  // the team-merge area (slot 0) is free again
-    if (fused) {
-      if (a.spin_ticks > 0) {
-        // merged after the page loop (its registers are free then)
-        if (tid == 0) s_tiles[n_tiles] = int3{t0, nrows, ncols};
-        ++n_tiles;
-      } else {
-        fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
-                                        reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
+    if constexpr (!WIDE) {
+      if (fused) {
+        if (a.spin_ticks > 0) {
+          // merged after the page loop (its registers are free then)
+          if (tid == 0) s_tiles[n_tiles] = int3{t0, nrows, ncols};
+          ++n_tiles;
+        } else {
+          fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
+                                          reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
+        }
       }
     }
     t0 += nrows;
     __syncthreads();  // LDS is reused by the next tile
   }
+  if constexpr (WIDE) return;
   for (int i = 0; i < n_tiles; ++i) {
     const int3 tl = s_tiles[i];
     const int ncols_i = tl.z;
@@ -1372,6 +1397,7 @@ using pgqa_detail::fail;
 // still have work.
 struct Plan {
   int kind;     // 0: per-wave kernel, 1: shared-page kernel
+  int wide = 0; // shared-page kernel with the teams on separate columns (prefill)
   int nsl;      // hd slices per column block (shared-page kernel)
   int cap;      // columns per tile
   int rmax;     // rows per tile
@@ -1394,21 +1420,26 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
 }
 
 // Prefill: tiles have many rows, so the shared-page kernel takes every hd
-// from 128 up with 64-column tiles (32 at hd 512), reading each page once per
-// 64 columns; hd 64 keeps the per-wave kernel's 16-column tiles.
+// from 128 up.  Its two teams take separate column blocks of one tile
+// (128 columns, 64 at hd 512: each page read once per tile) when a caller
+// tile's rows fill it -- at least 2 heads per kv head below hd 512 --, and
+// alternate pages of 64-column tiles otherwise; hd 64 keeps the per-wave
+// kernel's 16-column tiles.
 Plan make_prefill_plan(int64_t group, int64_t hd) {
   Plan p;
   p.kind = hd >= 128 ? 1 : 0;
   p.nsl = p.kind == 1 ? (hd == 512 ? 2 : 1) : 1;
-  p.cap = p.kind == 1 ? 16 * (kWaves / p.nsl) : 16;
+  const int team_cap = 16 * (kWaves / p.nsl);
+  p.wide = p.kind == 1 && 2 * team_cap <= kPrefillRowsPerTile * group;
+  p.cap = p.kind == 1 ? (p.wide ? 2 : 1) * team_cap : 16;
   p.rmax = group <= p.cap ? static_cast<int>(p.cap / group) : 1;
   p.hblocks = group <= p.cap ? 1 : static_cast<int>((group + p.cap - 1) / p.cap);
   return p;
 }
 
-template <int HD, int NSL>
+template <int HD, int NSL, bool WIDE = false>
 hipError_t launch_shared(const DecodeArgs &a, int64_t blocks, hipStream_t stream) {
-  hipLaunchKernelGGL((pgqa_shared_kernel<HD, NSL>), dim3(static_cast<unsigned>(blocks)), dim3(kSharedThreads), 0,
+  hipLaunchKernelGGL((pgqa_shared_kernel<HD, NSL, WIDE>), dim3(static_cast<unsigned>(blocks)), dim3(kSharedThreads), 0,
                      stream, a);
   return hipGetLastError();
 }
@@ -1417,6 +1448,14 @@ template <int HD>
 hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hipStream_t stream) {
   const dim3 grid(static_cast<unsigned>(blocks)), block(kThreads);
   if constexpr (HD >= 128) {
+    if (p.kind == 1 && p.wide) {
+      if constexpr (HD == 512) {
+        if (p.nsl == 2) return launch_shared<HD, 2, true>(a, blocks, stream);
+      } else {
+        if (p.nsl == 1) return launch_shared<HD, 1, true>(a, blocks, stream);
+      }
+      return hipErrorInvalidValue;
+    }
     if (p.kind == 1) {
       if (p.nsl == 2) return launch_shared<HD, 2>(a, blocks, stream);
       if constexpr (HD < 512) {

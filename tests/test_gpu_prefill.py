@@ -38,6 +38,9 @@ CASES = [
     # the per-wave kernel (hd 64) and the shared-page kernel at hd 128, group 8
     ("pf_hd64", 300, 8, 2, 64, 50),
     ("pf_hd128", 257, 16, 2, 128, 0),
+    # one head per kv head: the teams take alternate pages instead of
+    # separate column blocks
+    ("pf_mha", 200, 4, 4, 128, 0),
 ]
 
 
