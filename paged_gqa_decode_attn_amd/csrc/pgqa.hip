@@ -999,7 +999,9 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) uint16_t slot3[NP > 3 ? SLOT_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t slot4[NP > 4 ? SLOT_ELEMS : 8];
   __shared__ __attribute__((aligned(16))) uint16_t slot5[NP > 5 ? SLOT_ELEMS : 8];
-  __shared__ __attribute__((aligned(16))) f32x4 xscore[2 * kWaves][64];  // partial scores per wave
+  // partial scores per wave (WIDE: per wave and page of the pair, so the
+  // second page's exchange cannot overwrite the first's before it is read)
+  __shared__ __attribute__((aligned(16))) f32x4 xscore[(WIDE ? 4 : 2) * kWaves][64];
   __shared__ float xfer[2 * kWaves][16];
   __shared__ int s_is_last;
   __shared__ int3 s_tiles[64];  // tiles whose parallel merge follows the page loop (row, rows, columns)
@@ -1182,12 +1184,14 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       }
       if constexpr (NSL > 1) {
         // every wave of both teams takes part in the exchange barrier
-        if (work) xscore[wave][lane] = sc;
+        const int xr = WIDE ? 2 : 1, xp = WIDE ? pk : 0;  // rows per wave, this page's row
+        if (work) xscore[xr * wave + xp][lane] = sc;
         lds_barrier();
         if (work) {
-          sc = xscore[4 * team + cb * NSL][lane];
+          const int w0 = 4 * team + cb * NSL;
+          sc = xscore[xr * w0 + xp][lane];
   #pragma unroll
-          for (int s2 = 1; s2 < NSL; ++s2) sc += xscore[4 * team + cb * NSL + s2][lane];
+          for (int s2 = 1; s2 < NSL; ++s2) sc += xscore[xr * (w0 + s2) + xp][lane];
         }
       }
       if (!work || !active) return;
