@@ -200,3 +200,13 @@ def test_counter_capacity_refusal():
     with pytest.raises(pg.PgqaError) as ei:
         dw.run(2, counters=new_counters())
     assert ei.value.code == pg.ECAP
+
+
+def test_counter_capacity_full(counters):
+    """The largest fused call the counter buffer holds: 4096 rows x 1 kv head
+    (one merge unit per row) uses every counter; fused == separate bit for
+    bit, within the bound, counters zero afterwards."""
+    w = workloads.single_sequence("capfull", ctx=4200, rows=4096, nh=1, nkv=1, hd=64, window=300)
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    gate("capfull", dw, 3, counters, ref)
