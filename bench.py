@@ -66,10 +66,17 @@ def kv_bytes(w) -> int:
 
 
 def kernel_source_hash(source: str = "pgqa.hip") -> str:
-    h = hashlib.sha256()
-    with open(os.path.join(ROOT, "paged_gqa_decode_attn_amd", "csrc", source), "rb") as f:
-        h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of a kernel source's code: comments and blank lines are dropped,
+    so committed counter figures stay tied to the code they were taken on
+    and survive edits of the explanations only."""
+    import re
+
+    with open(os.path.join(ROOT, "paged_gqa_decode_attn_amd", "csrc", source)) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    lines = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+    code = "\n".join(line for line in lines if line.strip())
+    return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
 def committed_traffic(config: str):

@@ -25,7 +25,9 @@
 //     operand registers); narrow groups, batched decode.
 //   * pgqa_shared_kernel: up to 64-column tiles, 8 waves in two teams taking
 //     alternating pages staged in LDS by direct-to-LDS loads; groups of 8+
-//     with several rows, every hd-512 call, prefill.
+//     with several rows, every hd-512 call.  Its WIDE form (prefill) gives
+//     the teams separate column blocks of a tile twice as wide, both
+//     computing every page.
 //   * With S splits, each (tile, kv head, head block, split) workgroup writes
 //     an f32 partial (o, m, l); the merge (fixed order: 8 interleaved groups of
 //     splits, each an fma chain) runs in the last workgroup of the unit, in
