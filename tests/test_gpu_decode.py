@@ -174,6 +174,12 @@ def edge_workloads():
     cases.append(rng_seq("sh128s1", ctx=400, rows=5, nh=16, nkv=1, hd=128, window=77))
     cases.append(rng_seq("sh512s1", ctx=150, rows=9, nh=8, nkv=1, hd=512, window=0))
     cases.append(rng_seq("sh256g128", ctx=260, rows=2, nh=128, nkv=1, hd=256, window=0))
+    # block decode (non-causal inside the block): rows at positions 396..399
+    # all see keys up to 403, with and without a window anchored at qpos
+    for nm, win in (("block", 0), ("blockwin", 50)):
+        wb = rng_seq(nm, ctx=404, rows=4, nh=8, nkv=2, hd=128, window=win)
+        qb = np.arange(396, 400, dtype=np.int32)
+        cases.append(wb.replace(name=nm, qpos=qb, kv_last=np.full(4, 403, np.int32)))
     # an empty visible set (last key below the window start) -> zeros
     w3 = rng_seq("empty", ctx=200, rows=2, nh=4, nkv=1, hd=64, window=8)
     cases.append(w3.replace(name="empty", kv_last=np.array([150, 199], np.int32)))
