@@ -126,11 +126,14 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
         step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
         if flush == "read":
+            fev[i][0].record(stream)
             torch.sum(scratch, dim=0, out=sink)  # reads 1 GiB, writes 4 bytes
+            fev[i][1].record(stream)
         elif flush == "rw":
             scratch.add_(1)
         ev[i][0].record(stream)
@@ -146,6 +149,9 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     res["eff_gbs"] = b / (res["kernel_ms_mean"] * 1e-3) / 1e9
     res["eff_gbs_median"] = b / (res["kernel_ms_median"] * 1e-3) / 1e9
     res["rows_per_s"] = w.rows / (res["kernel_ms_mean"] * 1e-3)
+    if flush == "read":
+        # the eviction pass doubles as a read-bandwidth probe: torch.sum over 1 GiB of f32
+        res["read_probe_gbs"] = (1 << 30) / (min(a.elapsed_time(b) for a, b in fev) * 1e-3) / 1e9
     res["_w"], res["_out"] = w, out
     return res
 
@@ -377,9 +383,17 @@ def main():
                    "kv_bytes": res["kv_bytes"], "parallelism": "single-gpu"},
         "roofline": {"bound": "hbm", "achieved": round(res["eff_gbs"], 2), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(res["eff_gbs"] / HBM_PEAK_GBS, 4),
-                     "traffic": traffic, "kernel_ms": round(ms, 5)},
+                     "traffic": traffic, "kernel_ms": round(ms, 5),
+                     "kernel_ms_median": round(res["kernel_ms_median"], 5),
+                     "kernel_ms_min": round(res["kernel_ms_min"], 5)},
         "cpu_baseline": cpu,
     }
+    if "read_probe_gbs" in res:
+        # against what a plain framework reduction reads on this machine (labelled
+        # apart from the roofline, whose peak is the 8 TB/s specification)
+        line["read_probe"] = {"what": "torch.sum over 1 GiB f32 (the cache-eviction pass), best of the timed steps",
+                              "gbs": round(res["read_probe_gbs"], 1),
+                              "frac_of_probe": round(res["eff_gbs"] / res["read_probe_gbs"], 4)}
     if "rel_rms_sample" in res:
         line["rel_rms_sample"] = res["rel_rms_sample"]
     if secondary:
