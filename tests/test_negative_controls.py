@@ -133,3 +133,44 @@ def test_missing_counter_reset_is_caught():
     merged1, c = counter_protocol(c, 7, reset=False)
     merged2, c = counter_protocol(c, 7, reset=False)
     assert merged1 and not merged2 and c != 0  # second call never merges; counters not zero
+
+
+# ---- the QK-norm + RoPE prep gates (pegainfer pull request page #1002,
+# its negative controls: a paged address off by one must fail the
+# layout-address gate; every row pinned to row 0's window must fail the
+# decode == prefill gate) ----
+
+def _prep_pools(w):
+    kp, vp = w.zero_pools()
+    return oracle.qk_rope_prep(w.q_in, w.k_in, w.v_in, w.q_w, w.k_w, w.rope_cos, w.rope_sin, w.pos,
+                               w.block_table, w.page_origin, kp, vp, w.nh, w.nkv, w.hd, w.rotary_dim, w.eps,
+                               page_map=w.page_map)
+
+
+def test_prep_slot_off_by_one_is_caught():
+    """Writing each token one slot further (position + 1) lands values
+    outside the expected rows: the layout-address gate (exact zeros
+    elsewhere, the expected values in place) turns red."""
+    w = workloads.prep_prefill("negp", tokens=20, nh=2, nkv=1, hd=64, rotary_dim=32, p0=3)
+    _, kp, vp = _prep_pools(w)
+    # the same values one slot on: shift the positions, keep the rotary rows
+    shifted = w.replace(pos=(w.pos + 1).astype(np.int32),
+                        rope_cos=np.concatenate([w.rope_cos[:1], w.rope_cos]),
+                        rope_sin=np.concatenate([w.rope_sin[:1], w.rope_sin]))
+    _, kp2, vp2 = _prep_pools(shifted)
+    assert not np.array_equal(kp2, kp) and not np.array_equal(vp2, vp)
+    written = np.any(kp != 0, axis=-1)
+    assert np.any(np.any(kp2 != 0, axis=-1) & ~written)  # something landed outside the expected rows
+
+
+def test_prep_rows_pinned_to_row_zero_window_is_caught():
+    """The decode form with every token's origin pinned to token 0's (its
+    compressed window read for all rows) no longer equals the prefill form."""
+    w = workloads.prep_prefill("negq", tokens=40, nh=2, nkv=1, hd=64, rotary_dim=64, p0=5)
+    c = workloads.compress_windows(w)
+    q_ref, k_ref, v_ref = _prep_pools(w)
+    q_ok, k_ok, v_ok = _prep_pools(c)
+    assert np.array_equal(k_ok, k_ref) and np.array_equal(v_ok, v_ref)  # the gate passes when origins are read
+    pinned = c.replace(page_origin=np.full_like(c.page_origin, c.page_origin[0]))
+    _, k_bad, v_bad = _prep_pools(pinned)
+    assert not np.array_equal(k_bad, k_ref) or not np.array_equal(v_bad, v_ref)
