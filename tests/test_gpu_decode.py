@@ -199,6 +199,27 @@ def test_edge_cases(counters, w):
         assert not out[0].any()
 
 
+def merge_layout_workloads():
+    """Fused calls whose merge runs in parallel (2 MB or more of partials per
+    merge unit) in other shapes than C3's and C5's: 300 units of 4 rows (hd
+    512, group 8) in a launch larger than the device holds at once, so units
+    complete one after another while their waiting workgroups hold CUs; and
+    units of one column (MHA, hd 512; 16-column tiles, so parallel from 64
+    splits) with only 8 slices for 64 or more workgroups.  Split counts that
+    are not powers of two are included."""
+    rng_seq = workloads.single_sequence
+    return [(rng_seq("units300", ctx=1200, rows=300, nh=8, nkv=1, hd=512, window=0), (32, 37, 64)),
+            (rng_seq("col1", ctx=2000, rows=1, nh=2, nkv=2, hd=512, window=0), (64, 100, 125))]
+
+
+@pytest.mark.parametrize("w,splits", merge_layout_workloads(), ids=lambda x: getattr(x, "name", None))
+def test_parallel_merge_layouts(counters, w, splits):
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    for s in splits:
+        gate(w.name, dw, s, counters, ref)
+
+
 def test_counter_capacity_refusal():
     import paged_gqa_decode_attn_amd as pg
     w = workloads.single_sequence("cap", ctx=4200, rows=4097, nh=1, nkv=1, hd=64, window=0)
