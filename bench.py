@@ -79,9 +79,10 @@ def kernel_source_hash(source: str = "pgqa.hip") -> str:
     return hashlib.sha256(code.encode()).hexdigest()[:16]
 
 
-def committed_traffic(config: str):
-    """HBM bytes per launch from committed rocprofv3 counter runs, if they were
-    taken on the current kernel source."""
+def committed_traffic(config: str, mode: str = None, splits: int = None):
+    """HBM bytes per call from committed rocprofv3 counter runs, if they were
+    taken on the current kernel source (and, where the record names them, in
+    the same merge mode and split count)."""
     path = os.path.join(ROOT, "profiles", "traffic.json")
     try:
         with open(path) as f:
@@ -89,6 +90,10 @@ def committed_traffic(config: str):
     except (OSError, ValueError):
         return None
     if not rec or rec.get("kernel_sha") != kernel_source_hash(rec.get("kernel_source", "pgqa.hip")):
+        return None
+    if mode is not None and rec.get("mode", mode) != mode:
+        return None
+    if splits is not None and rec.get("splits", splits) != splits:
         return None
     return rec.get("bytes_per_launch")
 
@@ -346,7 +351,8 @@ def main():
             r.pop("_w"), r.pop("_out")
             secondary[name] = {"splits": r["splits"], "merge": mode, "us_per_call": round(r["kernel_ms_mean"] * 1e3, 2),
                                "GB/s": round(r["eff_gbs"], 1), "frac": round(r["eff_gbs"] / HBM_PEAK_GBS, 4),
-                               "rows_per_s": round(r["rows_per_s"], 1)}
+                               "rows_per_s": round(r["rows_per_s"], 1),
+                               "traffic": committed_traffic(name, mode, r["splits"])}
             torch.cuda.empty_cache()
         # paged prefill (MFMA-bound): the page's PA shape, and an 8K-token
         # causal context of the same head layout
@@ -363,7 +369,7 @@ def main():
             torch.cuda.empty_cache()
 
     ms = res["kernel_ms_mean"]
-    traffic = committed_traffic(args.config)
+    traffic = committed_traffic(args.config, args.mode, res["splits"])
     line = {
         "metric": "paged GQA decode attention: effective KV HBM GB/s and query rows/sec",
         "value": round(res["eff_gbs"], 2),

@@ -22,10 +22,10 @@
 //     yields the softmax denominators from the same MFMA.
 //   * pgqa_wave_kernel: 16-column tiles, 4 waves each taking every 4th page of
 //     the split with their own softmax state (K straight from HBM into MFMA
-//     operand registers); narrow groups, batched decode.
+//     operand registers); narrow groups, batched decode, one-row hd-512 decode.
 //   * pgqa_shared_kernel: up to 64-column tiles, 8 waves in two teams taking
 //     alternating pages staged in LDS by direct-to-LDS loads; groups of 8+
-//     with several rows, every hd-512 call.  Its WIDE form (prefill) gives
+//     with several rows, hd-512 tiles of more than 16 columns.  Its WIDE form (prefill) gives
 //     the teams separate column blocks of a tile twice as wide, both
 //     computing every page.
 //   * With S splits, each (tile, kv head, head block, split) workgroup writes
@@ -470,6 +470,12 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
 // softmax weights then stay below 2^kRescaleSlack.
 constexpr float kRescaleSlack = 8.f;
 
+// The parallel fused merge (defined with the combine kernel below).
+struct ChunkScratch;
+template <int HD, int NT>
+__device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
+                              ChunkScratch *cs, int *s_word);
+
 template <int HD>
 __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;   // QK^T MFMA steps (32 hd elements each)
@@ -667,7 +673,8 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   // Two register sets (hd <= 256): the next page's K and V are in flight while
   // the current page is computed; past the window's end its last page is
   // loaded again (already cached) so every step issues the same loads.  At
-  // hd 512 the registers hold one page only.
+  // hd 512 the registers hold one page only (one wave per SIMD; a second set
+  // would live in accumulation registers, and measured slower).
   for (int w0 = 0; w0 < nk; w0 += 128) {
     const int wn = min(128, nk - w0);
     fetch_window(w0);
@@ -770,7 +777,18 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   }
   if (!fused) return;
 
-  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]), &s_is_last);
+  // Large merges (hd 256 and 512 only; the host sets spin_ticks for those):
+  // all of the unit's workgroups together.  Otherwise the last one alone.
+  if constexpr (HD >= 256) {
+    if (a.spin_ticks > 0) {
+      __syncthreads();  // the V staging area is free for the merge scratch
+      claimed_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<ChunkScratch *>(&vtile[0][0]),
+                                  &s_is_last);
+      return;
+    }
+  }
+  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]),
+                            &s_is_last);
 }
 
 // ---- merge of one chunk of 32 hd elements of one (row, query head) ----
@@ -785,6 +803,7 @@ struct ChunkScratch {
   float w[kMaxSplits], l[kMaxSplits], red[kWaves], dgrp[kMergeGroups];
   float acc[kMergeGroups][32];
 };
+static_assert(sizeof(ChunkScratch) <= kWaves * kPage * (64 + 8) * 2, "chunk merge scratch must fit the per-wave kernel's V staging");
 template <class Load>
 __device__ __forceinline__ void merge_chunk32(const DecodeArgs &a, Load ld, int64_t th, int d0, int hd, int tid,
                                               bool live_chunk, ChunkScratch &cs) {
@@ -879,25 +898,29 @@ constexpr int64_t kParallelMergeBytes = int64_t(2) << 20;  // per-unit partials 
 constexpr int kClaimSpinTicks = 2000;                      // 20 us
 
 // One claimed slice: chunks 2 slice and 2 slice + 1 of the unit's outputs,
-// one per 256-thread half.
-template <int HD>
+// one per 256-thread half (a 256-thread workgroup merges them one after the
+// other, with the same per-element steps).
+template <int HD, int NT>
 __device__ __forceinline__ void merge_slice(const DecodeArgs &a, int t0, int kh, int hb, int nrows,
                                                       int nchunks, int cap, int slice, ChunkScratch *cs) {
   constexpr int per_col = HD / 32;
   const int tid = threadIdx.x;
-  const int half = tid >> 8;
-  const int c = 2 * slice + half;
-  const bool live = c < nchunks;
-  const int cc = live ? c : 2 * slice;
-  const Column rc = tile_column(cc / per_col, a.group, nrows, hb, cap);
-  const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-  merge_chunk32(a, LoadCoherent{}, th, (cc % per_col) * 32, HD, tid & 255, live, cs[half]);
+  const int half0 = NT == kThreads ? 0 : tid >> 8;
+#pragma unroll
+  for (int half = half0; half < (NT == kThreads ? 2 : half0 + 1); ++half) {
+    const int c = 2 * slice + half;
+    const bool live = c < nchunks;
+    const int cc = live ? c : 2 * slice;
+    const Column rc = tile_column(cc / per_col, a.group, nrows, hb, cap);
+    const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+    merge_chunk32(a, LoadCoherent{}, th, (cc % per_col) * 32, HD, tid & 255, live, cs[NT == kThreads ? 0 : half]);
+  }
 }
 
 template <int HD, int NT>
 __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
                               ChunkScratch *cs, int *s_word) {
-  static_assert(NT == 2 * kThreads, "two chunks per claim: one per 256-thread half");
+  static_assert(NT == kThreads || NT == 2 * kThreads, "a claim is two chunks: one per 256 threads, or both in turn");
   int32_t *w = a.counters + (t0 * a.nkv + kh) * a.hblocks + hb;
   const int S = a.splits;
   const int nchunks = ncols * (HD / 32);
@@ -940,7 +963,7 @@ __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int n
     __syncthreads();
     const int slice = *s_word;
     if (slice < 0) return;
-    merge_slice<HD>(a, t0, kh, hb, nrows, nchunks, cap, slice, cs);
+    merge_slice<HD, NT>(a, t0, kh, hb, nrows, nchunks, cap, slice, cs);
     __syncthreads();
     if (tid == 0) {
       const int done = __hip_atomic_fetch_add(w, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16;
@@ -1395,12 +1418,17 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
 
 using pgqa_detail::fail;
 
-// Which kernel runs and how rows are tiled, from the call's shapes only (so
-// calls that differ only in data -- merge mode, page placement -- run the same
-// code).  The shared-page kernel takes hd 512 and, from hd 128 up, tiles of
-// more than 16 columns; the per-wave kernel the rest.  With fewer columns than
-// the shared-page kernel's 64 the hd is cut into slices so that all 4 waves
-// still have work.
+// Which kernel runs and how rows are tiled, from the call's shapes and split
+// count only (so calls that differ only in data -- merge mode, page placement
+// -- run the same code).  The shared-page kernel takes, from hd 128 up, tiles
+// of more than 16 columns (groups of 8 or more; every group at hd 512); the
+// per-wave kernel the rest.  At hd 512 the per-wave kernel takes tiles of up
+// to 16 columns from 64 splits up (long spans, bandwidth-bound): its 4 waves
+// each keep a whole 32 KB K/V page in flight, twice what the shared-page
+// kernel's two-slot ring holds at hd 512, and from there on a fused merge is
+// always the parallel one.  Shorter hd-512 calls are latency-bound and stay on
+// the shared-page kernel.  With fewer columns than the shared-page kernel's
+// 64 the hd is cut into slices so that all 4 waves still have work.
 struct Plan {
   int kind;     // 0: per-wave kernel, 1: shared-page kernel
   int wide = 0; // shared-page kernel with the teams on separate columns (prefill)
@@ -1409,13 +1437,15 @@ struct Plan {
   int rmax;     // rows per tile
   int hblocks;  // head blocks per kv head
 };
-Plan make_plan(int64_t rows, int64_t group, int64_t hd) {
+constexpr int64_t kWave512MinSplits = 64;
+Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   Plan p;
   const int64_t cols = group <= 64 ? group * (rows < 64 / group ? rows : 64 / group) : 64;
   // groups of 8+ heads: several rows of one sequence fill a 64-column tile
   // (multi-row decode); narrower groups keep the per-wave kernel, whose
   // 16-column tiles waste nothing when every row has its own sequence
-  p.kind = hd == 512 || (hd >= 128 && cols > 16 && group >= 8) ? 1 : 0;
+  p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) ? 1 : 0;
+  if (hd == 512 && splits < kWave512MinSplits) p.kind = 1;
   p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
   if (p.kind == 1 && hd == 128 && p.nsl == 4) p.nsl = 2;  // hd 128 has 4 QK steps
   if (p.kind == 1 && hd == 512 && p.nsl == 1) p.nsl = 2;  // a whole hd-512 slice needs too many registers
@@ -1473,11 +1503,8 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
       return hipErrorInvalidValue;
     }
   }
-  if constexpr (HD < 512) {
-    hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
-    return hipGetLastError();
-  }
-  return hipErrorInvalidValue;
+  hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -1538,7 +1565,7 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(PGQA_EINVAL, "out must be 2-byte aligned");
 
   const int64_t group = nh / nkv;
-  const Plan plan = make_plan(rows, group, hd);
+  const Plan plan = make_plan(rows, group, hd, splits);
   // the per-wave kernel's workgroups each take one row (working only if it
   // starts a tile); the shared-page kernel's an rmax-aligned block of rows
   const int64_t grid_rows = plan.kind == 1 ? (rows + plan.rmax - 1) / plan.rmax : rows;
@@ -1583,9 +1610,11 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
 
   // The merge of one unit reads splits * cap * hd floats of partials: from
-  // 2 MB up the unit's workgroups merge it together (shared-page kernel),
-  // below that the last one to arrive merges it alone.
-  a.spin_ticks = counters != nullptr && splits > 1 && plan.kind == 1 && splits * plan.cap * hd * 4 >= kParallelMergeBytes
+  // 2 MB up the unit's workgroups merge it together (shared-page kernel, and
+  // the per-wave kernel from hd 256), below that the last one to arrive
+  // merges it alone.
+  a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind == 1 || hd >= 256) &&
+                         splits * plan.cap * hd * 4 >= kParallelMergeBytes
                      ? kClaimSpinTicks
                      : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
