@@ -88,8 +88,20 @@ def test_page_configs_and_page_map(counters, name):
 
 
 def test_c3_global_wide_head(counters):
+    """The heuristic's 128 splits (per-wave kernel at hd 512) and 32 (below
+    64 splits the shared-page kernel takes hd 512); a permuted pool behind a
+    page map gives the same bits in both."""
     dw = device("C3")
-    gate("C3", dw, dw.heuristic_splits(), counters, reference("C3"))
+    s_h = dw.heuristic_splits()
+    gate("C3", dw, s_h, counters, reference("C3"))
+    gate("C3", dw, 32, counters, reference("C3"))
+    dm = DeviceWorkload(workloads.with_page_map(workload("C3")))
+    for s in (32, s_h):
+        for cnt in (counters, None):
+            a = dw.host(dw.run(s, counters=cnt))
+            b = dm.host(dm.run(s, counters=cnt))
+            assert np.array_equal(a, b), ("C3 page map", s, cnt is None)
+    check_counters_zero(counters)
 
 
 @pytest.mark.parametrize("name", ["C4", "C4NAN"])
@@ -124,17 +136,50 @@ def test_c5_long_multirow_split_sweep(counters, name):
             assert np.array_equal(a, b), ("page map", s)
 
 
-@pytest.mark.parametrize("splits", [1, 2, 7, 64])
-def test_single_visible_key_is_exact(counters, splits):
-    """window = 1: the output is the V row of the query position, bit for bit."""
-    w = workload("PA").replace(window=1)
+@pytest.mark.parametrize("name,splits", [("PA", 1), ("PA", 2), ("PA", 7), ("PA", 64), ("C3", 7), ("C3", 64),
+                                         ("C3", 128), ("C5W0", 1), ("C5W0", 256)])
+def test_single_visible_key_is_exact(counters, name, splits):
+    """window = 1: the output is the V row of the query position, bit for bit,
+    in both merge modes (per-wave kernel: PA, and C3 from 64 splits;
+    shared-page kernel: C3 below 64 splits, C5)."""
+    w = workload(name).replace(window=1)
     dw = DeviceWorkload(w)
-    out = dw.host(dw.run(splits, counters=counters))
     g = w.nh // w.nkv
-    for t in range(w.rows):
-        p = int(w.qpos[t])
-        for h in range(w.nh):
-            assert np.array_equal(out[t, h], w.v_pool[int(w.block_table[p // 16]), h // g, p % 16])
+    for cnt in (counters, None):
+        out = dw.host(dw.run(splits, counters=cnt))
+        for t in range(w.rows):
+            p = int(w.qpos[t])
+            for h in range(w.nh):
+                assert np.array_equal(out[t, h], w.v_pool[int(w.block_table[p // 16]), h // g, p % 16]), \
+                    (name, splits, t, h)
+    check_counters_zero(counters)
+
+
+def bf16_within_one_ulp(a, b):
+    """bf16 bit patterns a and b are equal or adjacent values of one sign."""
+    a = a.astype(np.int32)
+    b = b.astype(np.int32)
+    same_sign = (a >> 15) == (b >> 15)
+    return bool(np.all(same_sign & (np.abs(a - b) <= 1)))
+
+
+@pytest.mark.parametrize("name,splits", [("PA", 8), ("C3", 32), ("C3", 128), ("C5W0", 256), ("C4", 3)])
+def test_constant_v_returns_that_row(counters, name, splits):
+    """Every key of a kv head carries the same V row: the softmax weights sum
+    to one, so every head of the group returns that row, whatever the scores
+    (checked to within one bf16 ulp: the weighted sum is rounded in f32)."""
+    w = workload(name)
+    rng = np.random.default_rng(2024)
+    vals = rng.uniform(0.25, 1.0, size=(w.nkv, w.hd)) * rng.choice([-1.0, 1.0], size=(w.nkv, w.hd))
+    vrow = (vals.astype(np.float32).view(np.uint32) >> 16).astype(np.uint16)
+    v = np.ascontiguousarray(np.broadcast_to(vrow[None, :, None, :], w.v_pool.shape))
+    dw = DeviceWorkload(w.replace(v_pool=v))
+    g = w.nh // w.nkv
+    expect = np.broadcast_to(vrow[np.arange(w.nh) // g][None], (w.rows, w.nh, w.hd))
+    for cnt in (counters, None):
+        out = dw.host(dw.run(splits, counters=cnt))
+        assert bf16_within_one_ulp(out, expect), (name, splits, cnt is None)
+    check_counters_zero(counters)
 
 
 def edge_workloads():
