@@ -119,9 +119,10 @@ int32_t pgqa_counter_capacity(void);
  * row sharing the origin are never read, so they may point anywhere -- e.g. at
  * a NaN-filled null page); the K/V rows of visible keys are finite.
  * Rows that share an origin and sit next to each other are processed together
- * and read each KV page once.  Bitwise properties: the result does not depend
- * on `counters` (fused merge == separate combine), nor on where pages live in
- * the pool (identity table == permuted pool behind a page map).
+ * and read each KV page once.  Bitwise properties, for a given split count:
+ * the result does not depend on `counters` (fused merge == separate combine),
+ * nor on where pages live in the pool (identity table == permuted pool behind
+ * a page map).  Different split counts may differ in the last bits.
  * `out` must not alias any input or `part`.  Calls that share `part` or
  * `counters` must not run concurrently.
  * Returns PGQA_OK, PGQA_EINVAL, PGQA_ECAP (counters given and
