@@ -252,12 +252,16 @@ def merge_layout_workloads():
     units of one column (MHA, hd 512; 16-column tiles, so parallel from 64
     splits) with only 8 slices for 64 or more workgroups; and 4 units of 8
     columns (2 rows x group 4, hd 512) in the per-wave kernel, merged by the
-    last workgroup at 32 splits and by all of them from 64.  Split counts
-    that are not powers of two are included."""
+    last workgroup at 32 splits and by all of them from 64; and a batch of 8
+    sequences at hd 512, group 2, in the per-wave kernel (16 units, 1024 or
+    more workgroups: rows taken longest first, several rounds of workgroups
+    while earlier units wait for their merges).  Split counts that are not powers
+    of two are included."""
     rng_seq = workloads.single_sequence
     return [(rng_seq("units300", ctx=1200, rows=300, nh=8, nkv=1, hd=512, window=0), (32, 37, 64)),
             (rng_seq("col1", ctx=2000, rows=1, nh=2, nkv=2, hd=512, window=0), (64, 100, 125)),
-            (rng_seq("g4x2", ctx=2100, rows=2, nh=16, nkv=4, hd=512, window=0), (32, 64, 131))]
+            (rng_seq("g4x2", ctx=2100, rows=2, nh=16, nkv=4, hd=512, window=0), (32, 64, 131)),
+            (workloads.batched("b512", nseq=8, lmin=600, lmax=3000, nh=4, nkv=2, hd=512, pad=16), (64, 100))]
 
 
 @pytest.mark.parametrize("w,splits", merge_layout_workloads(), ids=lambda x: getattr(x, "name", None))
