@@ -25,9 +25,10 @@
 //     operand registers); narrow groups, batched decode, one-row hd-512 decode.
 //   * pgqa_shared_kernel: up to 64-column tiles, 8 waves in two teams taking
 //     alternating pages staged in LDS by direct-to-LDS loads; groups of 8+
-//     with several rows, hd-512 tiles of more than 16 columns.  Its WIDE form (prefill) gives
-//     the teams separate column blocks of a tile twice as wide, both
-//     computing every page.
+//     with several rows, hd-512 tiles of more than 16 columns, and hd-512
+//     calls below 64 splits.  Its WIDE form (prefill) gives the teams
+//     separate column blocks of a tile twice as wide, both computing every
+//     page.
 //   * With S splits, each (tile, kv head, head block, split) workgroup writes
 //     an f32 partial (o, m, l); the merge (fixed order: 8 interleaved groups of
 //     splits, each an fma chain) runs in the last workgroup of the unit, in
@@ -975,7 +976,8 @@ __device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int n
 
 // ---------------------------------------------------------------------------
 // Shared-page kernel: tiles of up to 64 columns (e.g. 8 rows x 8 heads of one
-// sequence) and every hd-512 tile.  8 waves in two teams of 4; team t takes
+// sequence) and hd-512 tiles too wide for the per-wave kernel or in calls of
+// fewer than 64 splits.  8 waves in two teams of 4; team t takes
 // the split's pages 2j + t, so every SIMD holds two waves whose latency chains
 // (LDS reads, MFMA, exp) overlap.  Both teams stage their pages' K and V in
 // LDS with direct-to-LDS loads (global_load_lds_dwordx4) into a ring of NP
