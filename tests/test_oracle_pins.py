@@ -185,6 +185,32 @@ def test_brute_force_page_map_and_kv_last_below_qpos():
                 assert abs(mpmath.mpf(got64[t, h, d]) - w) <= 1e-12 * max(abs(w), 1e-30) + 1e-300
 
 
+@pytest.mark.parametrize("window", [0, 6])
+def test_brute_force_block_decode_kv_last_above_qpos(window):
+    """Block decode: rows at positions 36..39 of one sequence all see keys up to
+    43 (the last visible key is a separate argument from the query position),
+    with the window, when there is one, anchored at each row's own position."""
+    rng = np.random.default_rng(11 + window)
+    nh, nkv, hd, ctx = 4, 2, 8, 44
+    k = random_bits(rng, (ctx, nkv, hd), -2, 2)
+    v = random_bits(rng, (ctx, nkv, hd))
+    kp, vp, table, origins = scatter_pool([k], [v], nkv, hd, rng)
+    q = random_bits(rng, (4, nh, hd), -2, 2)
+    qpos = np.arange(36, 40, dtype=np.int32)
+    last = np.full(4, 43, np.int32)
+    got, got64 = oracle.decode_arrays(q, kp, vp, table, origins[[0, 0, 0, 0]], qpos, last, nh, nkv, hd,
+                                      window, want_f64=True)
+    want = brute_case(q, [k], [v], [0, 0, 0, 0], qpos, last, nh, nkv, window)
+    for t in range(4):
+        for h in range(nh):
+            for d in range(hd):
+                w = want[t][h][d]
+                assert abs(mpmath.mpf(got64[t, h, d]) - w) <= 1e-12 * max(abs(w), 1e-30) + 1e-300, (t, h, d)
+                bits, tie_dist = mp_to_bf16(w)
+                if tie_dist > 1e-9:
+                    assert got[t, h, d] == bits, (t, h, d)
+
+
 # --------------------------------------------------------------------------
 # closed forms
 # --------------------------------------------------------------------------
