@@ -1519,15 +1519,19 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
   const int64_t units = nseq * nkv;
   const int64_t pages = (kv_span + kPage - 1) / kPage;
-  // Two regimes, measured over split counts 1..256 on every configuration:
-  //  - long spans are bandwidth-bound: about 6 workgroups per CU on the 256
-  //    CUs (with the longest rows dispatched first, uneven lengths still
-  //    balance), at least 16 pages per split;
+  // Two regimes, measured over split counts 1..256 on every configuration
+  // and on sweeps of further lengths, head layouts and batch sizes:
+  //  - long spans are bandwidth-bound.  One sequence: about one workgroup per
+  //    CU on the 256 CUs (each workgroup's prologue and epilogue then come
+  //    once), at least 8 pages per split.  A batch: about 6 workgroups per CU
+  //    (with the longest rows dispatched first, uneven lengths still balance),
+  //    at most 16 splits, at least 16 pages per split;
   //  - short spans are latency-bound: about 64 workgroups in all, at least 4
   //    pages per split.
   // The larger of the two wins.
   auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
-  const int64_t s_long = std::min(cdiv(1536, units), pages / 16);
+  const int64_t s_long = nseq == 1 ? std::min(cdiv(256, units), pages / 8)
+                                   : std::min(std::min(cdiv(1536, units), int64_t(16)), pages / 16);
   const int64_t s_short = std::min(cdiv(64, units), pages / 4);
   int64_t s = std::max(s_long, s_short);
   if (s > kMaxSplits) s = kMaxSplits;

@@ -58,6 +58,31 @@ def test_choose_splits_range_and_determinism():
     assert pg.choose_splits(16384, 64, 8, 1) <= 4
 
 
+def test_choose_splits_on_the_measured_shapes():
+    """The split counts the sweeps found fastest (or within a few percent):
+    every target configuration, one-sequence calls at one workgroup per CU,
+    and batches of 4 to 64 sequences."""
+    # (kv_span, rows, nkv, rows_per_seq) -> splits
+    cases = {
+        (64, 1, 1, 1): 1,          # tiny decode
+        (1024, 4, 8, 4): 8,        # local sliding layer, window 1024
+        (32768, 1, 2, 1): 128,     # global layer, wide head (hd 512)
+        (16384, 64, 8, 1): 3,      # batched decode, 64 sequences
+        (131072, 8, 1, 8): 256,    # long multi-row, window 0
+        (4096, 8, 1, 8): 64,       # long multi-row, window 4096
+        (1024, 5, 8, 5): 8,        # the page's first parity shape
+        (700, 1, 2, 1): 11,        # the page's second parity shape
+        (16384, 1, 2, 1): 128,     # one row, hd 512, 16K: 31.6 us against 36.9 at 64
+        (65536, 1, 2, 1): 128,     # one row, hd 512, 64K: 58.7 us against 72.0 at 256
+        (32768, 1, 8, 1): 32,      # one row, hd 128, 8 kv heads: 34.8 us against 48.3 at 128
+        (16384, 8, 1, 8): 128,     # 8 rows x 8 heads, 16K: 28.4 us against 29.6 at 64
+        (16003, 4, 8, 1): 16,      # batch of 4: 37.8 us against 63.0 at 48
+        (16003, 16, 8, 1): 12,     # batch of 16
+    }
+    for args, want in cases.items():
+        assert pg.choose_splits(*args) == want, (args, pg.choose_splits(*args), want)
+
+
 FAKE = 0x10000  # never dereferenced: every call below is refused first
 
 
