@@ -5,30 +5,32 @@
  * benchmark's CPU-baseline leg may call this.  It shares no code, header or
  * constant with the HIP library and must never stand in for it.
  *
- * It is the definition written out, following the f64 reference in the span-02
- * GPU test page (respanai/span-02, engine/crates/kernels/tests/gpu.rs, function
- * `reference`):
- *   - scale 1.0: scores are the plain dot product q . k (no 1/sqrt(hd));
- *   - GQA: query head h reads kv head kh = h / (nh / nkv);
- *   - causal with an optional sliding window: key position p is visible to a
- *     row at position qpos iff lo <= p <= hi, lo = max(0, qpos + 1 - window)
- *     when window > 0 (else 0), hi = the row's last visible key (the page passes
- *     the query positions for it, so hi = qpos in every call it shows);
- *   - every bf16 input is widened exactly, dot products, exponentials, the
- *     normaliser and the weighted sum of V are all taken in f64:
- *       m = max_p s_p,  e_p = exp(s_p - m),  z = sum_p e_p,
- *       o_d = sum_p (e_p / z) * v_{p,d};
- *   - the f64 result is rounded once to bf16, round-to-nearest-even.  (The
- *     page's own `bf` helper truncates; rounding is the reading taken here, the
- *     two differ by at most one bf16 ulp.)
- * Addressing (same page, the pool layout and the `mapped_pool` helper):
- *   table entry = page_origin[row] + p / 16, physical page = block_table[entry]
- *   (then page_map[physical page] when a page map is given), element
- *   ((phys * nkv + kh) * 16 + p % 16) * hd + d of the K (or V) pool.
+ * What is computed is the definition of the span-02 GPU kernel test page
+ * (respanai/span-02, engine/crates/kernels/tests/gpu.rs): the quantities of its
+ * `reference` function, extended to the decode call's full contract (per-row
+ * page origins, a page map, a last-visible-key array).  For query row t and
+ * query head h:
+ *   - kv head kh = h / (nh / nkv) (grouped-query sharing);
+ *   - visible keys p: lo_t <= p <= hi_t, lo_t = max(0, qpos_t + 1 - window)
+ *     for a sliding layer (window > 0), else 0; hi_t = the row's last visible
+ *     key (the page passes the query positions there, so hi_t = qpos_t in
+ *     every call it shows);
+ *   - score s_p = q_t,h . k_p (scale 1.0, no 1/sqrt(hd));
+ *   - out_t,h = sum_p softmax(s)_p v_p = N / Z with, for any shift c,
+ *       N = sum_p exp(s_p - c) v_p,   Z = sum_p exp(s_p - c).
+ *     The shift c is the largest visible score, so no exponential overflows.
+ *   - every bf16 input is widened exactly; scores, exponentials, N and Z are
+ *     f64; out = N_d / Z is rounded once to bf16, nearest-even.  (The page's
+ *     own rounding helper truncates; nearest-even is the reading taken, the two
+ *     differ by at most one bf16 ulp.)
+ * Addressing (same page: pool layout [page][nkv][16][hd] and its page-map
+ * helper): the row's table starts at entry page_origin[t]; logical page
+ * j = p / 16 lives at physical page block_table[origin + j] (then
+ * page_map[that] when a map is given), slot p % 16.
  *
- * Sums run over p in increasing order, then over d in increasing order, with
- * no blocking, fusion or reordering.  Built without -ffast-math and with
- * -ffp-contract=off.
+ * The visible keys are walked page by page in increasing position; within a
+ * key the hd products are summed in increasing d.  No blocking, fusion or
+ * reordering beyond that.  Built without -ffast-math, with -ffp-contract=off.
  */
 #include <math.h>
 #include <stdint.h>
@@ -70,6 +72,62 @@ uint16_t oracle_f64_to_bf16(double x)
     return (uint16_t)(u >> 16);
 }
 
+/* One (row, head): the element offsets of its visible keys' K/V rows, then the
+ * shifted exponentials and the unnormalised sum.  Returns 0, or a negative
+ * addressing error. */
+static int attend_one(uint16_t *orow, double *ofrow, const uint16_t *qrow,
+                      const uint16_t *k_pool, const uint16_t *v_pool,
+                      const int32_t *block_table, int64_t table_len, int64_t origin,
+                      const int32_t *page_map, int64_t map_len, int64_t npages,
+                      int64_t nkv, int64_t kh, int64_t hd, int64_t lo, int64_t hi,
+                      int64_t *row_at, double *score, double *num)
+{
+    int64_t n = 0;
+    /* resolve the keys one page at a time: table entry -> (map) -> pool page */
+    for (int64_t page = lo >= 0 ? lo / ORACLE_PAGE : 0; hi >= lo && page <= hi / ORACLE_PAGE; ++page) {
+        const int64_t entry = origin + page;
+        if (entry < 0 || entry >= table_len)
+            return -2;
+        int64_t phys = block_table[entry];
+        if (page_map) {
+            if (phys < 0 || phys >= map_len)
+                return -4;
+            phys = page_map[phys];
+        }
+        if (phys < 0 || phys >= npages)
+            return -3;
+        const int64_t first = page * ORACLE_PAGE > lo ? page * ORACLE_PAGE : lo;
+        const int64_t last = page * ORACLE_PAGE + ORACLE_PAGE - 1 < hi ? page * ORACLE_PAGE + ORACLE_PAGE - 1 : hi;
+        for (int64_t p = first; p <= last; ++p)
+            row_at[n++] = ((phys * nkv + kh) * ORACLE_PAGE + p % ORACLE_PAGE) * hd;
+    }
+    double top = -INFINITY;
+    for (int64_t i = 0; i < n; ++i) {
+        double dot = 0.0;
+        for (int64_t d = 0; d < hd; ++d)
+            dot += bf16_to_f64(qrow[d]) * bf16_to_f64(k_pool[row_at[i] + d]);
+        score[i] = dot;
+        top = dot > top ? dot : top;
+    }
+    for (int64_t d = 0; d < hd; ++d)
+        num[d] = 0.0;
+    double z = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double e = exp(score[i] - top);
+        z += e;
+        const uint16_t *vrow = v_pool + row_at[i];
+        for (int64_t d = 0; d < hd; ++d)
+            num[d] += e * bf16_to_f64(vrow[d]);
+    }
+    for (int64_t d = 0; d < hd; ++d) {
+        const double o = n > 0 ? num[d] / z : 0.0;   /* nothing visible: 0 */
+        orow[d] = oracle_f64_to_bf16(o);
+        if (ofrow)
+            ofrow[d] = o;
+    }
+    return 0;
+}
+
 /* Error codes: 0 ok; -1 bad shape; -2 table index out of range; -3 page out of
  * range; -4 page-map index out of range; -5 out of memory. */
 int pgqa_oracle_decode(uint16_t *out, double *out_f64,
@@ -93,87 +151,59 @@ int pgqa_oracle_decode(uint16_t *out, double *out_f64,
 #endif
     for (int64_t job = 0; job < rows * nh; ++job) {
         const int64_t t = job / nh, h = job % nh;
-        const int64_t kh = h / group;
         const int64_t qp = qpos[t];
-        const int64_t lo = window > 0 ? (qp + 1 - window > 0 ? qp + 1 - window : 0) : 0;
+        int64_t lo = 0;
+        if (window > 0 && qp + 1 - window > 0)
+            lo = qp + 1 - window;
         const int64_t hi = kv_last[t];
-        const uint16_t *qrow = q + (t * nh + h) * hd;
-        uint16_t *orow = out + (t * nh + h) * hd;
-        double *o = calloc((size_t)hd, sizeof(double));
-        int64_t n = hi >= lo ? hi - lo + 1 : 0;
-        double *s = malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
-        int64_t *base = malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
-        if (!o || !s || !base) {
+        const int64_t n = hi >= lo ? hi - lo + 1 : 0;
+        int64_t *row_at = malloc((size_t)(n > 0 ? n : 1) * sizeof(int64_t));
+        double *score = malloc((size_t)(n > 0 ? n : 1) * sizeof(double));
+        double *num = malloc((size_t)hd * sizeof(double));
+        int rc = -5;
+        if (row_at && score && num)
+            rc = attend_one(out + job * hd, out_f64 ? out_f64 + job * hd : NULL, q + job * hd,
+                            k_pool, v_pool, block_table, table_len, page_origin[t], page_map, map_len,
+                            npages, nkv, h / group, hd, lo, hi, row_at, score, num);
+        if (rc != 0) {
 #ifdef _OPENMP
 #pragma omp atomic write
 #endif
-            status = -5;
-            free(o); free(s); free(base);
-            continue;
+            status = rc;
         }
-        int bad = 0;
-        /* Resolve every visible key's address: origin + p/16 -> table -> (map) -> pool. */
-        for (int64_t i = 0; i < n && !bad; ++i) {
-            const int64_t p = lo + i;
-            const int64_t entry = (int64_t)page_origin[t] + p / ORACLE_PAGE;
-            if (entry < 0 || entry >= table_len) { bad = -2; break; }
-            int64_t phys = block_table[entry];
-            if (page_map) {
-                if (phys < 0 || phys >= map_len) { bad = -4; break; }
-                phys = page_map[phys];
-            }
-            if (phys < 0 || phys >= npages) { bad = -3; break; }
-            base[i] = ((phys * nkv + kh) * ORACLE_PAGE + p % ORACLE_PAGE) * hd;
-        }
-        if (bad) {
-#ifdef _OPENMP
-#pragma omp atomic write
-#endif
-            status = bad;
-            free(o); free(s); free(base);
-            continue;
-        }
-        /* s_p = sum_d q_d k_{p,d} */
-        double m = -INFINITY;
-        for (int64_t i = 0; i < n; ++i) {
-            double acc = 0.0;
-            for (int64_t d = 0; d < hd; ++d)
-                acc += bf16_to_f64(qrow[d]) * bf16_to_f64(k_pool[base[i] + d]);
-            s[i] = acc;
-            if (acc > m)
-                m = acc;
-        }
-        /* e_p = exp(s_p - m), z = sum_p e_p */
-        double z = 0.0;
-        for (int64_t i = 0; i < n; ++i) {
-            s[i] = exp(s[i] - m);
-            z += s[i];
-        }
-        /* o_d = sum_p (e_p / z) v_{p,d}, p ascending for every d */
-        for (int64_t i = 0; i < n; ++i) {
-            const double w = s[i] / z;
-            for (int64_t d = 0; d < hd; ++d)
-                o[d] += w * bf16_to_f64(v_pool[base[i] + d]);
-        }
-        for (int64_t d = 0; d < hd; ++d) {
-            orow[d] = oracle_f64_to_bf16(o[d]);
-            if (out_f64)
-                out_f64[(t * nh + h) * hd + d] = o[d];
-        }
-        free(o); free(s); free(base);
+        free(row_at);
+        free(score);
+        free(num);
     }
     return status;
 }
 
-/* rel-RMS of a against reference b, both bf16 bit patterns, accumulated in f64:
- * sqrt(sum (a-b)^2 / max(sum b^2, 1e-30)) -- the span-02 test's `rel_rms`. */
+/* Root-mean-square difference of a from the reference b, relative to the
+ * root-mean-square of b, both bf16 bit patterns, in f64.  A zero reference
+ * gives 0 when a equals it and +inf otherwise. */
+static double rel_rms_span(const uint16_t *a, const uint16_t *b, int64_t n)
+{
+    double diff2 = 0.0, ref2 = 0.0;
+    for (int64_t i = 0; i < n; ++i) {
+        const double y = bf16_to_f64(b[i]);
+        const double dv = bf16_to_f64(a[i]) - y;
+        diff2 += dv * dv;
+        ref2 += y * y;
+    }
+    if (ref2 == 0.0)
+        return diff2 == 0.0 ? 0.0 : INFINITY;
+    return sqrt(diff2 / ref2);
+}
+
 double pgqa_oracle_rel_rms(const uint16_t *a, const uint16_t *b, int64_t n)
 {
-    double num = 0.0, den = 0.0;
-    for (int64_t i = 0; i < n; ++i) {
-        const double x = bf16_to_f64(a[i]), y = bf16_to_f64(b[i]);
-        num += (x - y) * (x - y);
-        den += y * y;
-    }
-    return sqrt(num / (den > 1e-30 ? den : 1e-30));
+    return rel_rms_span(a, b, n);
+}
+
+/* The same measure for each of nvec consecutive vectors of len elements
+ * (e.g. every (row, head) output row of hd values). */
+void pgqa_oracle_rel_rms_each(const uint16_t *a, const uint16_t *b, int64_t nvec, int64_t len, double *out)
+{
+    for (int64_t i = 0; i < nvec; ++i)
+        out[i] = rel_rms_span(a + i * len, b + i * len, len);
 }

@@ -380,4 +380,25 @@ def test_rel_rms_hand_values():
     assert oracle.rel_rms(np.zeros(64, np.uint16), one) == pytest.approx(1.0)
     up = np.full(64, 0x3F81, np.uint16)            # 1 + 2^-7
     assert oracle.rel_rms(up, one) == pytest.approx(2.0 ** -7, rel=1e-12)
-    assert oracle.rel_rms(one, np.zeros(64, np.uint16)) == pytest.approx(math.sqrt(64 / 1e-30))
+    zero = np.zeros(64, np.uint16)
+    assert oracle.rel_rms(zero, zero) == 0.0                  # zero reference, matched
+    assert oracle.rel_rms(one, zero) == math.inf               # zero reference, missed
+
+
+def test_rel_rms_each_hand_values():
+    """One value per last-axis vector: a vector of 1.0 with one element at
+    1 + 2^-7 among n gives 2^-7 / sqrt(n); a vector of 2.0 against 1.0 gives 1;
+    a NaN makes its own vector's value NaN and no other's."""
+    one = np.full((3, 2, 8), 0x3F80, np.uint16)
+    a = one.copy()
+    a[0, 1, 5] = 0x3F81
+    a[2, 0, :] = 0x4000                                 # 2.0
+    a[1, 1, 3] = 0x7FC0                                 # NaN
+    e = oracle.rel_rms_each(a, one)
+    assert e.shape == (3, 2)
+    assert e[0, 1] == pytest.approx(2.0 ** -7 / math.sqrt(8), rel=1e-12)
+    assert e[2, 0] == pytest.approx(1.0, rel=1e-12)
+    assert math.isnan(e[1, 1])
+    ok = np.ones((3, 2), bool)
+    ok[0, 1] = ok[2, 0] = ok[1, 1] = False
+    assert np.all(e[ok] == 0.0)
