@@ -102,7 +102,7 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     import torch
 
     import paged_gqa_decode_attn_amd as pg
-    from tests.gpu_util import DeviceWorkload  # upload helper only
+    from workloads.device import DeviceWorkload  # upload helper only
 
     t0 = time.perf_counter()
     w = workloads.make(name)
@@ -131,14 +131,11 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
         step()
     torch.cuda.synchronize()
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
-    fev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
     torch.cuda.synchronize()
     wall0 = time.perf_counter()
     for i in range(steps):
         if flush == "read":
-            fev[i][0].record(stream)
             torch.sum(scratch, dim=0, out=sink)  # reads 1 GiB, writes 4 bytes
-            fev[i][1].record(stream)
         elif flush == "rw":
             scratch.add_(1)
         ev[i][0].record(stream)
@@ -154,10 +151,68 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
     res["eff_gbs"] = b / (res["kernel_ms_mean"] * 1e-3) / 1e9
     res["eff_gbs_median"] = b / (res["kernel_ms_median"] * 1e-3) / 1e9
     res["rows_per_s"] = w.rows / (res["kernel_ms_mean"] * 1e-3)
-    if flush == "read":
-        # the eviction pass doubles as a read-bandwidth probe: torch.sum over 1 GiB of f32
-        res["read_probe_gbs"] = (1 << 30) / (min(a.elapsed_time(b) for a, b in fev) * 1e-3) / 1e9
     res["_w"], res["_out"] = w, out
+    return res
+
+
+def _probe_lib():
+    import ctypes
+
+    path = os.path.join(ROOT, "paged_gqa_decode_attn_amd", "libpgqa_probe.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")
+    h = ctypes.CDLL(path)
+    h.pgqa_probe_read.restype = ctypes.c_int
+    h.pgqa_probe_read.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                                  ctypes.c_void_p, ctypes.c_void_p]
+    return h
+
+
+def read_probe(sizes=(("contiguous_2GiB", 2 << 30, 0), ("contiguous_128MiB", 128 << 20, 0),
+                      ("scattered_4KB_2GiB", 2 << 30, 1)), steps=5, warmup=2):
+    """The streaming-read ceiling of this GPU with the decode kernels' load form
+    (16-byte nontemporal loads into registers; csrc/read_probe.hip): for each
+    pattern, a sweep of grid sizes and loads in flight, each timed with HIP
+    events over single launches after a 1 GiB eviction read; the best mean per
+    pattern is reported."""
+    import torch
+
+    h = _probe_lib()
+    stream = torch.cuda.current_stream()
+    big = torch.empty(max(b for _, b, _ in sizes) // 4, dtype=torch.float32, device="cuda")
+    big.fill_(1.0)
+    scratch = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+    sink_t = torch.zeros((), dtype=torch.float32, device="cuda")
+    res = {}
+    for name, nbytes, scatter in sizes:
+        best = None
+        for blocks in (256, 512, 1024, 2048, 4096):
+            for unroll in (4, 8, 16):
+                if scatter and unroll == 16:
+                    continue
+                sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
+                run = lambda: h.pgqa_probe_read(big.data_ptr(), nbytes, blocks, unroll, scatter, sink.data_ptr(),
+                                                stream.cuda_stream)
+                if run() != 0:
+                    raise RuntimeError(f"read probe refused {name} blocks={blocks} unroll={unroll}")
+                for _ in range(warmup - 1):
+                    run()
+                ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(steps)]
+                for a, b in ev:
+                    torch.sum(scratch, dim=0, out=sink_t)  # evict L2 and the Infinity Cache
+                    a.record(stream)
+                    run()
+                    b.record(stream)
+                torch.cuda.synchronize()
+                ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                if best is None or gbs > best["GB/s"]:
+                    best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 2), "workgroups": blocks,
+                            "loads_in_flight_per_lane": unroll, "bytes": nbytes}
+        res[name] = best
+        log(f"[bench] read probe {name}: {best}")
+    del big, scratch
+    torch.cuda.empty_cache()
     return res
 
 
@@ -177,7 +232,7 @@ def run_prefill(w, steps, warmup, flush):
     import torch
 
     import paged_gqa_decode_attn_amd as pg
-    from tests.gpu_util import DeviceWorkload, dev_i32  # upload helpers only
+    from workloads.device import DeviceWorkload, dev_i32  # upload helpers only
 
     dw = DeviceWorkload(w)
     t0, tn = pg.make_tiles(w.page_origin, pg.prefill_rows_per_tile(w.hd))
@@ -218,7 +273,7 @@ def run_prep(w, steps, warmup, flush):
     """Time pgqa_qk_rope_prep over every token of w into resident pools."""
     import torch
 
-    from tests.gpu_util import DevicePrep  # upload helper only
+    from workloads.device import DevicePrep  # upload helper only
 
     d = DevicePrep(w)
     shape = (w.npages, w.nkv, 16, w.hd)
@@ -292,8 +347,14 @@ def main():
     ap.add_argument("--no-secondary", action="store_true",
                     help="skip the short runs of the other target configurations")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-read-probe", action="store_true", help="skip the streaming-read probe sweep")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only run a 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
+    ap.add_argument("--read-probe", action="store_true",
+                    help="only run the streaming-read probe (csrc/read_probe.hip); one JSON line")
+    ap.add_argument("--probe-pattern", default="",
+                    help="with --read-probe: one pattern only, as NAME:BYTES:SCATTER:WORKGROUPS:UNROLL "
+                         "(for counter runs), e.g. c:1073741824:0:1024:8")
     ap.add_argument("--prep", default="",
                     help="only time the QK-norm + RoPE prep on this prep workload (e.g. R128P8K); one JSON line")
     args = ap.parse_args()
@@ -313,6 +374,21 @@ def main():
         torch.cuda.synchronize()
         log("[bench] copied 1 GiB 5 times")
         return
+    if args.read_probe:
+        if args.probe_pattern:
+            name, nbytes, scatter, blocks, unroll = args.probe_pattern.split(":")
+            h = _probe_lib()
+            buf = torch.ones(int(nbytes) // 4, dtype=torch.float32, device="cuda")
+            sink = torch.empty(int(blocks), dtype=torch.int32, device="cuda")
+            for _ in range(args.steps):
+                rc = h.pgqa_probe_read(buf.data_ptr(), int(nbytes), int(blocks), int(unroll), int(scatter),
+                                       sink.data_ptr(), torch.cuda.current_stream().cuda_stream)
+                assert rc == 0, rc
+            torch.cuda.synchronize()
+            print(json.dumps({"read_probe": name, "bytes_per_launch": int(nbytes), "launches": args.steps}), flush=True)
+            return
+        print(json.dumps({"read_probe": read_probe()}), flush=True)
+        return
     if args.prep:
         r = run_prep(workloads.make_prep(args.prep), args.steps, args.warmup, not args.no_flush)
         print(json.dumps({"prep": args.prep, **r}), flush=True)
@@ -330,6 +406,14 @@ def main():
         gpu_rows = out.cpu().numpy().view(np.uint16)[rows]
         res["rel_rms_sample"] = oracle.rel_rms(gpu_rows, ref)
         log(f"[bench] cpu baseline {cpu}; rel_rms on sample {res['rel_rms_sample']:.3e}")
+        # the oracle on one host thread, over the whole global wide-head
+        # workload (one row, 32768 keys, 16/2/512)
+        c3 = workloads.make("C3")
+        t0 = time.perf_counter()
+        oracle.decode(c3, threads=1)
+        el = time.perf_counter() - t0
+        cpu["one_thread_C3"] = {"seconds": round(el, 4), "rows_per_s": round(c3.rows / el, 3),
+                                "GB/s": round(kv_bytes(c3) / el / 1e9, 3), "threads": 1}
 
     if args.all:
         for name in ("C1", "C2", "C3", "C5W0", "C5W4096", "PA", "PB"):
@@ -368,6 +452,7 @@ def main():
             secondary[pname] = run_prep(workloads.make_prep(wname), 20, 3, not args.no_flush)
             torch.cuda.empty_cache()
 
+    probe = None if args.no_read_probe else read_probe()
     ms = res["kernel_ms_mean"]
     traffic = committed_traffic(args.config, args.mode, res["splits"])
     line = {
@@ -394,12 +479,15 @@ def main():
                      "kernel_ms_min": round(res["kernel_ms_min"], 5)},
         "cpu_baseline": cpu,
     }
-    if "read_probe_gbs" in res:
-        # against what a plain framework reduction reads on this machine (labelled
-        # apart from the roofline, whose peak is the 8 TB/s specification)
-        line["read_probe"] = {"what": "torch.sum over 1 GiB f32 (the cache-eviction pass), best of the timed steps",
-                              "gbs": round(res["read_probe_gbs"], 1),
-                              "frac_of_probe": round(res["eff_gbs"] / res["read_probe_gbs"], 4)}
+    if probe:
+        # against what a plain streaming read reaches on this machine with the
+        # kernels' own load form (labelled apart from the roofline, whose peak
+        # is the 8 TB/s specification)
+        ref_pat = "scattered_4KB_2GiB" if args.config.upper().startswith("C4") else "contiguous_128MiB"
+        line["read_probe"] = {"what": "csrc/read_probe.hip: 16-byte nontemporal loads, every byte once, "
+                                      "best of a grid/in-flight sweep", **probe,
+                              "frac_of_probe": round(res["eff_gbs"] / probe[ref_pat]["GB/s"], 4),
+                              "probe_pattern_compared": ref_pat}
     if "rel_rms_sample" in res:
         line["rel_rms_sample"] = res["rel_rms_sample"]
     if secondary:

@@ -125,7 +125,8 @@ int32_t pgqa_counter_capacity(void);
  * a page map).  Different split counts may differ in the last bits.
  * `out` must not alias any input or `part`.  Calls that share `part` or
  * `counters` must not run concurrently.
- * Returns PGQA_OK, PGQA_EINVAL, PGQA_ECAP (counters given and
+ * Returns PGQA_OK, PGQA_EINVAL (also for shapes whose launch grid would
+ * exceed 2^32 - 1 threads), PGQA_ECAP (counters given and
  * rows * nkv * ceil(nh / nkv / 16) > pgqa_counter_capacity()) or PGQA_ELAUNCH.
  */
 int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool,
@@ -225,6 +226,18 @@ int pgqa_qk_rope_prep(void *q_out, void *k_pool, void *v_pool, const void *q_in,
                       const int32_t *pos, const int32_t *block_table, const int32_t *page_origin,
                       const int32_t *page_map, int64_t tokens, int64_t nh, int64_t nkv, int64_t hd,
                       int64_t rotary_dim, float eps, void *stream);
+
+/*
+ * Test hook for the fused merge's give-up path (no page defines it).  When one
+ * merge unit's partials reach 2 MB, the unit's workgroups merge it together,
+ * each waiting at most `ticks` ticks of the GPU's 100 MHz real-time counter
+ * for the unit's last arrival before it leaves the merge to the others (the
+ * last arrival merges whatever nobody took).  Any ticks >= 1 gives the same
+ * result bit for bit; it only changes how the work is shared.  0 restores the
+ * default (2000 ticks = 20 us).  Applies to the calls enqueued after it, from
+ * any thread.  Returns the previous setting, or PGQA_EINVAL for ticks < 0.
+ */
+int32_t pgqa_set_merge_wait_ticks(int32_t ticks);
 
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pgqa_last_error(void);

@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         h.pgqa_make_tiles.argtypes = [p, i64, i64, p, p, i64]
         h.pgqa_attn_prefill.restype = ctypes.c_int
         h.pgqa_attn_prefill.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
+        h.pgqa_set_merge_wait_ticks.restype = ctypes.c_int32
+        h.pgqa_set_merge_wait_ticks.argtypes = [ctypes.c_int32]
         h.pgqa_qk_rope_prep.restype = ctypes.c_int
         h.pgqa_qk_rope_prep.argtypes = [p] * 14 + [i64, i64, i64, i64, i64, ctypes.c_float, p]
         _lib = h
@@ -76,6 +78,15 @@ def decode_part_bytes(rows: int, nh: int, splits: int, hd: int) -> int:
 
 def counter_capacity() -> int:
     return int(lib().pgqa_counter_capacity())
+
+
+def set_merge_wait_ticks(ticks: int) -> int:
+    """Test hook (``pgqa_set_merge_wait_ticks``): bound of the fused merge's
+    waits, in 100 MHz ticks (0 = default); returns the previous setting."""
+    rc = int(lib().pgqa_set_merge_wait_ticks(ticks))
+    if rc < 0:
+        raise PgqaError(rc, "ticks must be >= 0")
+    return rc
 
 
 def last_error() -> str:

@@ -40,6 +40,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <atomic>
 #include <climits>
 #include <cstdarg>
 #include <cstdint>
@@ -897,6 +898,9 @@ __global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, in
 // with fewer helpers.
 constexpr int64_t kParallelMergeBytes = int64_t(2) << 20;  // per-unit partials from which the merge goes parallel
 constexpr int kClaimSpinTicks = 2000;                      // 20 us
+// Bound of the parallel merge's waits for the calls that follow, set by
+// pgqa_set_merge_wait_ticks (0: kClaimSpinTicks).
+std::atomic<int> g_merge_wait_ticks{0};
 
 // One claimed slice: chunks 2 slice and 2 slice + 1 of the unit's outputs,
 // one per 256-thread half (a 256-thread workgroup merges them one after the
@@ -1548,6 +1552,11 @@ int32_t pgqa_counter_capacity(void) { return kCounterCap; }
 
 const char *pgqa_last_error(void) { return pgqa_detail::error_text(); }
 
+int32_t pgqa_set_merge_wait_ticks(int32_t ticks) {
+  if (ticks < 0) return PGQA_EINVAL;
+  return g_merge_wait_ticks.exchange(ticks, std::memory_order_relaxed);
+}
+
 int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,
                      const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
                      const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
@@ -1581,7 +1590,14 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
                 (long long)(rows * nkv * ((group + 15) / 16)), kCounterCap);
   if (rows * nh * (hd > 128 ? hd / 128 : 1) > INT_MAX) return fail(PGQA_EINVAL, "rows * nh too large");
   const int64_t blocks = grid_rows * nkv * plan.hblocks * splits;
-  if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
+  // every grid is checked before anything is enqueued: a launch holds at most
+  // 2^32 - 1 threads in all
+  const int64_t block_threads = plan.kind == 1 ? kSharedThreads : kThreads;
+  if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
+    return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
+  const int64_t combine_blocks = rows * nh * (hd / 32);
+  if (splits > 1 && !counters && combine_blocks * kThreads > int64_t(UINT32_MAX))
+    return fail(PGQA_EINVAL, "combine grid of %lld workgroups too large", (long long)combine_blocks);
 
   DecodeArgs a;
   a.out = static_cast<uint16_t *>(out);
@@ -1619,9 +1635,10 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   // 2 MB up the unit's workgroups merge it together (shared-page kernel, and
   // the per-wave kernel from hd 256), below that the last one to arrive
   // merges it alone.
+  const int wait_ticks = g_merge_wait_ticks.load(std::memory_order_relaxed);
   a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind == 1 || hd >= 256) &&
                          splits * plan.cap * hd * 4 >= kParallelMergeBytes
-                     ? kClaimSpinTicks
+                     ? (wait_ticks > 0 ? wait_ticks : kClaimSpinTicks)
                      : 0;
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t err;
@@ -1687,7 +1704,9 @@ int pgqa_attn_prefill(void *out, const void *q, const void *k_pool, const void *
   const Plan plan = make_prefill_plan(group, hd);
   const int64_t nsub = (kPrefillRowsPerTile + plan.rmax - 1) / plan.rmax;
   const int64_t blocks = ntiles * nsub * nkv * plan.hblocks;
-  if (blocks > INT_MAX) return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
+  const int64_t block_threads = plan.kind == 1 ? kSharedThreads : kThreads;
+  if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
+    return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
 
   DecodeArgs a;
   a.out = static_cast<uint16_t *>(out);

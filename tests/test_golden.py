@@ -55,9 +55,13 @@ def test_counter_buffer_matches_the_page():
 
 
 def test_tolerances_in_the_gpu_tests():
-    """The GPU parity tests gate decode and prefill at the page's bounds."""
-    for fname, key in (("test_gpu_decode.py", "decode_rel_rms_bound"), ("test_gpu_prefill.py", "prefill_rel_rms_bound")):
-        text = open(os.path.join(HERE, fname)).read()
-        m = re.search(r"^TOL = ([0-9.e+-]+)$", text, re.M)
-        assert m, fname
-        assert float(m.group(1)) == val(key), fname
+    """The GPU parity tests gate decode and prefill at the page's bounds: they
+    take the gate's bound (tests/gates.py) and nothing looser."""
+    text = open(os.path.join(HERE, "gates.py")).read()
+    m = re.search(r"^TOL = ([0-9.e+-]+)$", text, re.M)
+    assert m
+    assert float(m.group(1)) == val("decode_rel_rms_bound") == val("prefill_rel_rms_bound")
+    for fname in ("test_gpu_decode.py", "test_gpu_prefill.py", "test_gpu_edges.py"):
+        src = open(os.path.join(HERE, fname)).read()
+        assert "from tests.gates import TOL, per_head" in src, fname
+        assert not re.search(r"^TOL = ", src, re.M), fname

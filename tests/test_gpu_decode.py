@@ -2,7 +2,8 @@
 bitwise gates of the span-02 GPU test page (fused merge == separate combine;
 identity pool == permuted pool behind a page map with a NaN null page).
 
-Tolerance: rel-RMS < 1e-2 against the oracle (the page's bound for decode).
+Tolerance: rel-RMS < 1e-2 against the oracle (the page's bound for decode),
+required of every (row, head) output vector on its own.
 """
 import functools
 import sys
@@ -15,13 +16,13 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-torch = pytest.importorskip("torch")
-if not torch.cuda.is_available():  # pragma: no cover - CPU container
-    pytest.skip("needs a GPU", allow_module_level=True)
+from tests.gpu_env import need_gpu  # noqa: E402
 
+need_gpu()
+import torch  # noqa: E402
+
+from tests.gates import TOL, per_head  # noqa: E402
 from tests.gpu_util import DeviceWorkload, new_counters  # noqa: E402
-
-TOL = 1e-2
 
 
 def say(*a):
@@ -58,9 +59,9 @@ def gate(name, dw, splits, cnt, ref):
     check_counters_zero(cnt)
     sep = dw.host(dw.run(splits, counters=None))
     assert np.array_equal(fused, sep), f"{name}: fused merge != separate combine at splits={splits}"
-    e = oracle.rel_rms(fused, ref)
-    say(f"[gpu] {name} splits={splits} rel_rms={e:.3e}")
-    assert e < TOL, (name, splits, e)
+    whole, worst, at = per_head(fused, ref)
+    say(f"[gpu] {name} splits={splits} rel_rms={whole:.3e} worst (row, head) {at}: {worst:.3e}")
+    assert worst < TOL, (name, splits, "worst (row, head)", at, worst)
     return fused
 
 
@@ -84,7 +85,7 @@ def test_page_configs_and_page_map(counters, name):
         x = dw.host(dw.run(s2, counters=counters))
         y = dm.host(dm.run(s2, counters=counters))
         assert np.array_equal(x, y), (name, s2)
-        assert oracle.rel_rms(x, reference(name)) < TOL
+        assert per_head(x, reference(name))[1] < TOL
 
 
 def test_c3_global_wide_head(counters):
@@ -126,7 +127,7 @@ def test_c5_long_multirow_split_sweep(counters, name):
         sep = dw.host(dw.run(s, counters=None))
         assert np.array_equal(fused, sep), (name, s)
         if s in (1, 2, 7, 64, 255, 256):
-            assert oracle.rel_rms(fused, ref) < TOL, (name, s)
+            assert per_head(fused, ref)[1] < TOL, (name, s)
     check_counters_zero(counters)
     if name == "C5W4096":
         dm = DeviceWorkload(workloads.with_page_map(workload(name)))
@@ -289,3 +290,24 @@ def test_counter_capacity_full(counters):
     dw = DeviceWorkload(w)
     ref = oracle.decode(w)
     gate("capfull", dw, 3, counters, ref)
+
+
+@pytest.mark.parametrize("name,splits", [("C3", 128), ("C5W0", 256), ("C5W4096", 64)])
+def test_fused_merge_when_waiters_give_up(counters, name, splits):
+    """The parallel fused merge with every wait bounded at one tick: the
+    waiting workgroups leave almost at once and the last arrival merges what
+    nobody took.  Same bits as the separate combine, counters back at zero,
+    and the default bound restored afterwards."""
+    import paged_gqa_decode_attn_amd as pg
+    dw = device(name)
+    sep = dw.host(dw.run(splits, counters=None))
+    prev = pg.set_merge_wait_ticks(1)
+    try:
+        for _ in range(2):
+            say(f"[gpu] {name} splits={splits} fused, waits of one tick")
+            fused = dw.host(dw.run(splits, counters=counters))
+            check_counters_zero(counters)
+            assert np.array_equal(fused, sep), (name, splits)
+    finally:
+        pg.set_merge_wait_ticks(prev)
+    assert per_head(sep, reference(name))[1] < TOL

@@ -12,14 +12,14 @@ import workloads
 
 pytestmark = pytest.mark.gpu
 
-torch = pytest.importorskip("torch")
-if not torch.cuda.is_available():  # pragma: no cover - CPU container
-    pytest.skip("needs a GPU", allow_module_level=True)
+from tests.gpu_env import need_gpu  # noqa: E402
+
+need_gpu()
+import torch  # noqa: E402
 
 import paged_gqa_decode_attn_amd as pg  # noqa: E402
+from tests.gates import TOL, per_head  # noqa: E402
 from tests.gpu_util import DeviceWorkload  # noqa: E402
-
-TOL = 1e-2
 
 
 def say(*a):
@@ -52,16 +52,16 @@ def test_prefill_matches_oracle_and_page_map(case):
     dw = DeviceWorkload(w)
     got = dw.host(dw.prefill())
     ref = oracle.decode(w)
-    e = oracle.rel_rms(got, ref)
-    say(f"[gpu] prefill {name}: rel_rms={e:.3e}")
-    assert e < TOL, (name, e)
+    whole, worst, at = per_head(got, ref)
+    say(f"[gpu] prefill {name}: rel_rms={whole:.3e} worst (row, head) {at}: {worst:.3e}")
+    assert worst < TOL, (name, at, worst)
     # the page's mapped pool for prefill keeps every page live
     wm = workloads.with_page_map(w, first_live=0)
     dm = DeviceWorkload(wm)
     assert np.array_equal(dm.host(dm.prefill()), got), f"{name}: page-map pool differs"
     # the same rows through decode agree within the bound too
     dec = dw.host(dw.run(1))
-    assert oracle.rel_rms(dec, ref) < TOL
+    assert per_head(dec, ref)[1] < TOL
 
 
 def test_prefill_batched_sequences_and_tile_sizes():
@@ -78,11 +78,11 @@ def test_prefill_batched_sequences_and_tile_sizes():
     dw = DeviceWorkload(w)
     ref = oracle.decode(w)
     full = dw.host(dw.prefill())
-    assert oracle.rel_rms(full, ref) < TOL
+    assert per_head(full, ref)[1] < TOL
     for rpt in (1, 5, 16, 64):
         tiles = pg.make_tiles(w.page_origin, rpt)
         got = dw.host(dw.prefill(tiles=tiles))
-        assert oracle.rel_rms(got, ref) < TOL, rpt
+        assert per_head(got, ref)[1] < TOL, rpt
 
 
 def test_prefill_skips_tiles_outside_the_rows():
@@ -95,5 +95,5 @@ def test_prefill_skips_tiles_outside_the_rows():
     out = torch.full((w.rows, w.nh, w.hd), 0x1234, dtype=torch.int16, device="cuda")
     got = dw.host(dw.prefill(tiles=(t0, tn), out=out))
     ref = oracle.decode(w)
-    assert oracle.rel_rms(got[:90], ref[:90]) < TOL
+    assert per_head(got[:90], ref[:90])[1] < TOL
     assert np.all(got[90:] == 0x1234)

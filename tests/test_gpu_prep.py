@@ -17,12 +17,17 @@ few roundings.
 """
 import numpy as np
 import pytest
-import torch
 
-import oracle
-import paged_gqa_decode_attn_amd as pg
-import workloads
-from tests.gpu_util import DevicePrep, DeviceWorkload
+from tests.gpu_env import need_gpu
+
+need_gpu()
+import torch  # noqa: E402
+
+import oracle  # noqa: E402
+import paged_gqa_decode_attn_amd as pg  # noqa: E402
+import workloads  # noqa: E402
+from tests.gates import TOL, per_head  # noqa: E402
+from tests.gpu_util import DevicePrep, DeviceWorkload  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
@@ -160,4 +165,4 @@ def test_prep_then_decode():
     got = d.host(d.run(d.heuristic_splits()))
     ref = oracle.decode_arrays(q_o[-rows:], kp_o, vp_o, w.block_table, np.zeros(rows, np.int32), qpos, qpos,
                                w.nh, w.nkv, w.hd, 0)
-    assert oracle.rel_rms(got, ref) < 1e-2
+    assert per_head(got, ref)[1] < TOL

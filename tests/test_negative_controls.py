@@ -12,8 +12,7 @@ import pytest
 
 import oracle
 import workloads
-
-TOL = 1e-2
+from tests.gates import TOL, per_head
 
 
 def red(ref, got):
@@ -60,6 +59,67 @@ def test_rows_pinned_to_row_zero_window_is_caught():
     # row 0 itself is unchanged; every other row moves
     assert np.array_equal(bad[0], ref[0])
     assert red(ref[1:], bad[1:])
+
+
+# ---- window edges, through the per-(row, head) gate the GPU tests use ----
+
+def red_per_head(ref, got):
+    return not (per_head(got, ref)[1] < TOL)
+
+
+@pytest.fixture(scope="module")
+def one_row_batch():
+    w = workloads.edge_batch("neg_eb", nseq=6, lmin=200, lmax=1500, nh=8, nkv=4, hd=128, window=150)
+    return w, oracle.decode(w)
+
+
+def test_edge_slip_on_one_row_sequences_is_caught(one_row_batch):
+    """One key too many below the window start (window + 1) or above the last
+    key (kv_last + 1) reads a NaN sentinel."""
+    w, ref = one_row_batch
+    assert per_head(ref, ref)[1] == 0.0
+    assert red_per_head(ref, oracle.decode(w.replace(window=w.window + 1)))
+    assert red_per_head(ref, oracle.decode(w.replace(kv_last=w.kv_last + 1)))
+    # one row alone slipping is enough
+    last = w.kv_last.copy()
+    last[3] += 1
+    bad = oracle.decode(w.replace(kv_last=last))
+    assert red_per_head(ref[3:4], bad[3:4]) and not red_per_head(np.delete(ref, 3, 0), np.delete(bad, 3, 0))
+
+
+@pytest.mark.parametrize("name", ["PA", "C2"])
+def test_edge_slip_inside_a_shared_sequence_is_caught(name):
+    """Rows of one sequence at the page's window of 1024: row t taking in
+    lo_t - 1 (seen legitimately by row t - 1) or kv_last_t + 1 (seen by row
+    t + 1) picks up the key aimed at it, and the aimed-at head of every kv
+    group turns red -- a one-key slip that a whole-output gate can average
+    away."""
+    w = workloads.plant_edges(workloads.make(name))
+    ref = oracle.decode(w)
+    g = w.nh // w.nkv
+    for t in range(1, w.rows):  # lower edge: start one key early (same last key)
+        qp = w.qpos.copy()
+        qp[t] -= 1
+        bad = oracle.decode(w.replace(qpos=qp))
+        e = oracle.rel_rms_each(bad, ref)
+        aimed = [kh * g + t % g for kh in range(w.nkv)]
+        assert np.all(e[t, aimed] > 0.1), (name, "lower", t, e[t, aimed])
+        assert np.all(np.delete(e, t, 0) == 0.0)
+    for t in range(w.rows - 1):  # upper edge: one key past the last
+        last = w.kv_last.copy()
+        last[t] += 1
+        bad = oracle.decode(w.replace(kv_last=last))
+        e = oracle.rel_rms_each(bad, ref)
+        aimed = [kh * g + t % g for kh in range(w.nkv)]
+        assert np.all(e[t, aimed] > 0.1), (name, "upper", t, e[t, aimed])
+
+
+def test_rows_pinned_to_row_zero_window_at_the_page_window_is_caught():
+    """The C2 shape (window 1024): every row using row 0's range."""
+    w = workloads.plant_edges(workloads.make("C2"))
+    ref = oracle.decode(w)
+    pinned = w.replace(qpos=np.full_like(w.qpos, w.qpos[0]), kv_last=np.full_like(w.kv_last, w.kv_last[0]))
+    assert red_per_head(ref[1:], oracle.decode(pinned)[1:])
 
 
 def test_window_off_by_one_is_caught():

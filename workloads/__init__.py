@@ -447,3 +447,99 @@ def make_prep(name: str) -> PrepWorkload:
 
 
 PREP_NAMES = ("R256F", "R256P", "R512KV", "R128D", "R64D")
+
+
+# ---------------------------------------------------------------------------
+# Window-edge sentinels.  The visibility rule (span-02 GPU test page,
+# ``reference``: causal, and inside a sliding window when one is set) decides
+# which keys of a loaded page a row may read.  These inputs make a one-key slip
+# at either edge of any row's visible range change that row's output by O(1):
+#   * a slot of a loaded page that no row of the sequence can see holds NaN in
+#     K and V (reading it, or multiplying its V by a zero weight, gives NaN);
+#   * a slot just outside row t's range (lo_t - 1 or hi_t + 1) that another
+#     row of the same sequence does see holds a key aimed at one head of row t
+#     in every kv group: K = c * sign(q[t, h]), c = 4 * max|K| of the pool.
+#     Row t's score for it would be c * sum|q[t, h]|, far above every real
+#     score, so including it turns head h of row t into that key's V row.
+# ---------------------------------------------------------------------------
+
+def row_ranges(w: Workload):
+    """Per row: (lo, hi) visible key range (hi < lo: nothing visible)."""
+    lo = np.where(w.window > 0, np.maximum(0, w.qpos.astype(np.int64) + 1 - w.window), 0)
+    return [(int(lo[t]), int(w.kv_last[t])) for t in range(w.rows)]
+
+
+def plant_edges(w: Workload, name: Optional[str] = None) -> Workload:
+    """``w`` with NaN in every slot of a loaded page that no row of its
+    sequence sees and a dominant key at every window edge that another row of
+    the sequence sees (see above).  Rows that share a page origin share a
+    sequence; a sequence's loaded pages are those from its lowest visible key's
+    page to its highest's.  Returns a new workload (pools copied)."""
+    k = w.k_pool.copy()
+    v = w.v_pool.copy()
+    g = w.nh // w.nkv
+    kmag = float(np.abs(bf16_bits_to_f32(w.k_pool[np.isfinite(bf16_bits_to_f32(w.k_pool))])).max(initial=1.0))
+    c = np.float32(2.0 ** np.ceil(np.log2(4.0 * kmag)))  # a power of two: exact in bf16
+    rng = row_ranges(w)
+    seqs = {}
+    for t in range(w.rows):
+        seqs.setdefault(int(w.page_origin[t]), []).append(t)
+
+    def slot(origin, p):
+        phys = int(w.block_table[origin + p // PAGE])
+        if w.page_map is not None:
+            phys = int(w.page_map[phys])
+        return phys, p % PAGE
+
+    for origin, rows in seqs.items():
+        live = [(rng[t][0], rng[t][1]) for t in rows if rng[t][1] >= rng[t][0]]
+        if not live:
+            continue
+        p_lo = min(a for a, _ in live) // PAGE * PAGE
+        p_hi = (max(b for _, b in live) // PAGE + 1) * PAGE - 1
+        seen = np.zeros(p_hi - p_lo + 1, bool)
+        for a, b in live:
+            seen[a - p_lo:b - p_lo + 1] = True
+        for p in range(p_lo, p_hi + 1):
+            if not seen[p - p_lo]:
+                phys, s = slot(origin, p)
+                k[phys, :, s, :] = BF16_QNAN
+                v[phys, :, s, :] = BF16_QNAN
+        taken = set()
+        for t in rows:
+            a, b = rng[t]
+            if b < a:
+                continue
+            for e in (a - 1, b + 1):
+                if e < p_lo or e > p_hi or not seen[e - p_lo] or e in taken:
+                    continue
+                taken.add(e)
+                phys, s = slot(origin, e)
+                for kh in range(w.nkv):
+                    h = kh * g + t % g
+                    neg = (w.q[t, h] & 0x8000) != 0
+                    row = np.where(neg, -c, c).astype(np.float32)
+                    k[phys, kh, s, :] = (row.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    return w.replace(name=name or w.name + "+edges", k_pool=k, v_pool=v,
+                     note=w.note + ", window-edge sentinels")
+
+
+def edge_batch(name: str, nseq: int, lmin: int, lmax: int, nh: int, nkv: int, hd: int, window: int,
+               len_seed: int = 4242) -> Workload:
+    """A batch of one-row sequences whose visible ranges start and end inside a
+    page (so the slots at lo - 1 and hi + 1 sit in pages the kernels load):
+    row s sits a few keys before its sequence's last written slot, chosen so
+    that hi % 16 != 15 and, with a window, lo % 16 != 0.  With window-edge
+    sentinels planted."""
+    b = batched(name, nseq=nseq, lmin=lmin, lmax=lmax, nh=nh, nkv=nkv, hd=hd, window=window,
+                len_seed=len_seed, pad=16)
+    qp = b.qpos.astype(np.int64).copy()
+    for s in range(nseq):
+        for back in range(1, 40):
+            x = int(b.qpos[s]) - back
+            lo = x + 1 - window if window > 0 else 1
+            if x >= 0 and x % PAGE != PAGE - 1 and (window <= 0 or (lo > 0 and lo % PAGE != 0)):
+                qp[s] = x
+                break
+    qp = qp.astype(np.int32)
+    return plant_edges(b.replace(qpos=qp, kv_last=qp.copy()), name=name)
