@@ -20,20 +20,25 @@
 //     v_mfma_f32_16x16x16_bf16, so P V needs no shuffle of P; V reaches the B
 //     operand through the LDS transpose read; a column of ones appended to V
 //     yields the softmax denominators from the same MFMA.
-//   * pgqa_wave_kernel: 16-column tiles, 4 waves each taking every 4th page of
-//     the split with their own softmax state (K straight from HBM into MFMA
-//     operand registers); narrow groups, batched decode, one-row hd-512 decode.
+//   * pgqa_wave_kernel (hd 64 to 256): 16-column tiles, 4 waves each taking
+//     every 4th page of the split with their own softmax state (K straight
+//     from HBM into MFMA operand registers); narrow groups, batched decode.
+//   * pgqa_slice_kernel (hd 512, tiles of up to 16 columns): the 4 waves take
+//     every page, each a quarter of hd, with RING pages in flight per wave in
+//     registers; the partial scores are summed through LDS, so all waves hold
+//     one softmax state and no cross-wave merge is needed; one-row and
+//     few-row decode of wide heads.
 //   * pgqa_shared_kernel: up to 64-column tiles, 8 waves in two teams taking
 //     alternating pages staged in LDS by direct-to-LDS loads; groups of 8+
-//     with several rows, hd-512 tiles of more than 16 columns, and hd-512
-//     calls below 64 splits.  Its WIDE form (prefill) gives the teams
-//     separate column blocks of a tile twice as wide, both computing every
-//     page.
+//     with several rows, hd-512 tiles of more than 16 columns.  Its WIDE form
+//     (prefill) gives the teams separate column blocks of a tile twice as
+//     wide, both computing every page.
 //   * With S splits, each (tile, kv head, head block, split) workgroup writes
 //     an f32 partial (o, m, l); the merge (fixed order: 8 interleaved groups of
 //     splits, each an fma chain) runs in the last workgroup of the unit, in
-//     all of the unit's workgroups together (large merges), or in the separate
-//     combine kernel -- the same arithmetic per element, so the same bits.
+//     all of the unit's workgroups together (large merges: each its own
+//     32-element blocks, one wave per block), or in the separate combine
+//     kernel -- the same arithmetic per element, so the same bits.
 //   * Masked scores are replaced by -inf with a select and V rows of tokens no
 //     column can see are zeroed with a select, so a NaN page or NaN slot outside
 //     every window cannot leak into the result.
@@ -100,8 +105,8 @@ struct DecodeArgs {
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
   int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
-  int spin_ticks;  // shared-page kernel, fused merge: > 0 selects the parallel (claimed-slice) merge and
-                   // bounds each workgroup's wait for the unit's last arrival (100 MHz ticks)
+  int spin_ticks;  // fused merge: > 0 selects the parallel (owned-block) merge and bounds each
+                   // workgroup's wait for the unit's last arrival (100 MHz ticks)
   // prefill: caller-made tiles (runs of rows on one sequence, at most
   // kPrefillRowsPerTile rows each), cut into nsub sub-tiles of rmax rows;
   // NULL for decode
@@ -473,10 +478,9 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
 constexpr float kRescaleSlack = 8.f;
 
 // The parallel fused merge (defined with the combine kernel below).
-struct ChunkScratch;
 template <int HD, int NT>
-__device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
-                              ChunkScratch *cs, int *s_word);
+__device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
+                            int *s_word);
 
 template <int HD>
 __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
@@ -784,8 +788,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   if constexpr (HD >= 256) {
     if (a.spin_ticks > 0) {
       __syncthreads();  // the V staging area is free for the merge scratch
-      claimed_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<ChunkScratch *>(&vtile[0][0]),
-                                  &s_is_last);
+      owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, &s_is_last);
       return;
     }
   }
@@ -793,188 +796,523 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
                             &s_is_last);
 }
 
-// ---- merge of one chunk of 32 hd elements of one (row, query head) ----
-// 256 threads: thread (g, e) = (tid / 32, tid % 32) owns element e of the
-// chunk for the splits s = g mod 8.  Every load -- the (m, l) of all splits
-// and the thread's partial elements -- is issued before any is used, so the
-// merge costs one memory round trip.  Both the combine kernel and the
-// parallel fused merge run exactly this per element.  `live` false: the
-// threads only take part in the barriers.
-constexpr int kCombineSplits = kMaxSplits / kMergeGroups;  // splits per thread
-struct ChunkScratch {
-  float w[kMaxSplits], l[kMaxSplits], red[kWaves], dgrp[kMergeGroups];
-  float acc[kMergeGroups][32];
-};
-static_assert(sizeof(ChunkScratch) <= kWaves * kPage * (64 + 8) * 2, "chunk merge scratch must fit the per-wave kernel's V staging");
-template <class Load>
-__device__ __forceinline__ void merge_chunk32(const DecodeArgs &a, Load ld, int64_t th, int d0, int hd, int tid,
-                                              bool live_chunk, ChunkScratch &cs) {
-  const int g = tid >> 5, e = tid & 31;
-  const int S = a.splits;
-  const float *ml = a.part_ml + th * S * 2;
-  const float *o = a.part_o + th * S * hd + d0 + e;
-  float m = 0.f, l = 0.f;
-  float v[kCombineSplits];
-  if (live_chunk) {
-    const int sm = min(tid, S - 1);
-    m = ld(ml + 2 * sm);
-    l = ld(ml + 2 * sm + 1);
+// ---------------------------------------------------------------------------
+// hd-sliced kernel: tiles of up to 16 columns at large hd (one-row and
+// few-row decode of wide heads).  The 4 waves of a workgroup split hd into 4
+// slices and all walk every page of the split: wave w loads, for each page,
+// only its slice of K and V (HD / 4 elements of each of the 16 tokens), so a
+// page costs a wave HD / 8 registers of K and as many of V, and RING pages are
+// in flight per wave at once -- loads of page k + RING are issued as soon as
+// page k's registers are consumed (K after the scores, V after its staging).
+// Each wave's partial scores (its slice of q . k) go through LDS; every wave
+// adds the 4 slices in the same order, so all 4 hold the same scores and the
+// same softmax state, and each accumulates P V for its own hd slice.  At the
+// end no cross-wave merge is needed: wave w owns output elements
+// [w HD / 4, (w + 1) HD / 4) of every column.
+// ---------------------------------------------------------------------------
+template <int HD>
+__global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
+  constexpr int HS = HD / kWaves;  // hd slice of one wave
+  constexpr int KS = HS / 32;      // QK^T MFMA steps over the slice
+  constexpr int DS = HS / 16;      // PV output blocks of the slice
+  constexpr int VL = HS / 32;      // 16-byte V loads per lane per page
+  constexpr int RING = 3;          // pages in flight per wave (RING + 1 register sets)
+  constexpr int VSTR = HS + 8;     // LDS row stride of a staged V slice (elements)
+  // The reference max follows every new column max (no slack): the largest
+  // weight of the row is then exactly 1 before bf16 rounding, which keeps the
+  // rounding of the weights out of the dominant term (measured: worst
+  // per-head error against the f64 oracle 1.45e-3 instead of 2.2e-3 on a
+  // 32K-key global layer, at the same speed).
+  constexpr float SLACK = 0.f;
+  __shared__ __attribute__((aligned(16))) uint16_t vtile[kWaves][kPage * VSTR];
+  // partial scores of every wave, two buffers used in turn: a wave can only
+  // write one again after passing the next exchange's barrier, which every
+  // wave reaches after reading it
+  __shared__ __attribute__((aligned(16))) f32x4 xs[2][kWaves][64];
+  __shared__ float xfer[kWaves][16];
+  __shared__ int s_is_last;
+  static_assert(KS >= 1 && DS >= 1, "the hd-sliced kernel needs hd >= 128");
+  static_assert(sizeof(FusedScratch<kThreads>) <= sizeof(vtile), "merge scratch must fit the V staging area");
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int ln = lane & 15;
+  const int lc = lane >> 4;
+  const int h0 = wave * HS;  // first hd element of this wave's slice
+
+  int b = blockIdx.x;
+  const int split = b % a.splits;
+  b /= a.splits;
+  const int hb = b % a.hblocks;
+  b /= a.hblocks;
+  const int kh = b % a.nkv;
+  const int t0 = row_of_rank(a, b / a.nkv, lane);
+
+  // ---- Q of this wave's slice for every possible column (first round trip) ----
+  const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
+  bf16x8 qop[KS];
+  {
+    const bool q_in = col0.on && t0 + col0.row < a.rows;
+    const uint16_t *qrow =
+        a.q + (static_cast<int64_t>(t0 + (q_in ? col0.row : 0)) * a.nh + kh * a.group + col0.head) * HD + h0;
 #pragma unroll
-    for (int i = 0; i < kCombineSplits; ++i) v[i] = ld(o + static_cast<int64_t>(min(g + kMergeGroups * i, S - 1)) * hd);
-  }
-  const bool live = live_chunk && tid < S && l > 0.f;
-  float mx = live ? m : -INFINITY;
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-  if ((tid & 63) == 0) cs.red[tid >> 6] = mx;
-  __syncthreads();
-  mx = fmaxf(fmaxf(cs.red[0], cs.red[1]), fmaxf(cs.red[2], cs.red[3]));
-  cs.w[tid] = live ? fast_exp2(m - mx) : 0.f;
-  cs.l[tid] = l;
-  __syncthreads();
-  if (tid < kMergeGroups) {
-    float dg = 0.f;
-    for (int s = tid; s < S; s += kMergeGroups) {
-      const float ws = cs.w[s];
-      dg = ws != 0.f ? __builtin_fmaf(ws, cs.l[s], dg) : dg;
-    }
-    cs.dgrp[tid] = dg;
-  }
-  float num = 0.f;
-  if (live_chunk) {
-#pragma unroll
-    for (int i = 0; i < kCombineSplits; ++i) {
-      const int s = g + kMergeGroups * i;
-      if (s < S) {
-        const float ws = cs.w[s];
-        num = ws != 0.f ? __builtin_fmaf(ws, v[i], num) : num;
+    for (int j = 0; j < KS; ++j) {
+      if (q_in) {
+        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[j] = __builtin_bit_cast(bf16x8, z);
       }
     }
   }
-  cs.acc[g][e] = num;
-  __syncthreads();
-  if (live_chunk && tid < 32) {
-    float n = 0.f, den = 0.f;
+  const Tile tile = tile_rows(a, t0, lane);
+  if (!tile.lead) return;
+  const int origin = tile.origin;
+  const int nrows = tile.nrows;
+  int pbeg, pend;
+  split_range(tile, split, a.splits, pbeg, pend);
+
+  const Column col = tile_column(ln, a.group, nrows, hb, 16);
+  const int col_lo = __shfl(tile.lo_l, col.row);
+  const int col_hi_any = __shfl(tile.hi_l, col.row);
+  const int col_hi = col.on ? col_hi_any : -1;
+  if (!col.on) {
 #pragma unroll
-    for (int gg = 0; gg < kMergeGroups; ++gg) {
-      n += cs.acc[gg][tid];
-      den += cs.dgrp[gg];
+    for (int j = 0; j < KS; ++j) {
+      u32x4 z = {0u, 0u, 0u, 0u};
+      qop[j] = __builtin_bit_cast(bf16x8, z);
     }
-    a.out[th * hd + d0 + tid] = f32_to_bf16_rne(den > 0.f ? n / den : 0.f);
   }
-  __syncthreads();  // the scratch is reused by the next chunk
+
+  float m_run = -INFINITY;
+  f32x4 oacc[DS];
+  f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int u = 0; u < DS; ++u) oacc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+  const s16x4 ones = {0x3f80, 0x3f80, 0x3f80, 0x3f80};
+  const int64_t kv_head_off = static_cast<int64_t>(kh) * kPage * HD + h0;
+  const int64_t page_elems = static_cast<int64_t>(a.nkv) * kPage * HD;
+  uint16_t *vt = vtile[wave];
+  const uint16_t *vtr = vt + (4 * lc + (ln >> 2)) * VSTR + 4 * (ln & 3);
+
+  // Physical pages of the split, 128 per window in two VGPRs per lane.  Page
+  // ids are looked up only for the page being requested, which runs RING
+  // pages ahead.  When it leaves the window, the next window is fetched and
+  // waited for (every load in flight drains once per 128 pages): the window
+  // registers are then never waited on inside the page loop.
+  const int nk = pend - pbeg;
+  int cur0 = 0, cur1 = 0, cur_w = 0;
+  int xpar = 0;  // score-exchange buffer in use (flips on every exchange; uniform)
+  auto fetch_window = [&](int w0) {
+    int ph[2];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int k = w0 + 64 * h + lane;
+      ph[h] = 0;
+      if (k < nk) {
+        ph[h] = a.block_table[origin + pbeg + k];
+        if (a.page_map) ph[h] = a.page_map[ph[h]];
+      }
+    }
+    cur0 = ph[0];
+    cur1 = ph[1];
+    cur_w = w0;
+    wait_all_memory();
+  };
+  auto phys_of = [&](int k) -> int {
+    const int off = k - cur_w;  // 0 .. 127
+    return __builtin_amdgcn_readlane(off < 64 ? cur0 : cur1, off & 63);
+  };
+  // The loads of page k into a register set.  With real false (a refill past
+  // the last page) load j of every lane reads the 16 bytes at j * 16 of the
+  // window's first page instead (a page of the split): the same number of
+  // load instructions, distinct (so none is merged into another) but all
+  // within one cache line, and the data is never used.
+  auto load_k = [&](int k, bool real, bf16x8(&kr)[KS]) {
+    const uint16_t *kp = a.k_pool + static_cast<int64_t>(phys_of(real ? k : cur_w)) * page_elems + kv_head_off;
+#pragma unroll
+    for (int j = 0; j < KS; ++j)
+      kr[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const bf16x8 *>(kp + (real ? ln * HD + (4 * j + lc) * 8 : 8 * j)));
+  };
+  auto load_v = [&](int k, bool real, u32x4(&vr)[VL]) {
+    const uint16_t *vp = a.v_pool + static_cast<int64_t>(phys_of(real ? k : cur_w)) * page_elems + kv_head_off;
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const int e = (j * 64 + lane) * 8;  // element of the [16][HS] slice
+      const int tok = e / HS;
+      vr[j] = __builtin_nontemporal_load(
+          reinterpret_cast<const u32x4 *>(vp + (real ? tok * HD + (e - tok * HS) : 8 * (KS + j))));
+    }
+  };
+
+  // Step k: first the register set that page k - 1 used (consumed in the
+  // previous step) is refilled with page k + RING, then page k is computed
+  // from its own set (kr, vr).  Every step -- also the steps past the last
+  // page, which only refill -- issues the same loads in the same order, and a
+  // refill never shares a basic block with the last use of its registers, so
+  // the compiler's counted waits leave RING pages in flight.  All 4 waves take
+  // every page, so the per-page decisions (visibility, skip) are the same in
+  // all of them.
+  auto page = [&](int k, bf16x8(&kr)[KS], u32x4(&vr)[VL], bf16x8(&kf)[KS], u32x4(&vf)[VL]) {
+    const int p = pbeg + k;
+    const int kn = k + RING;  // >= 0
+    const bool real = kn < nk;
+    if (real && kn - cur_w >= 128) fetch_window(cur_w + 128);  // the page to request leaves the window
+    load_k(kn, real, kf);
+    load_v(kn, real, vf);
+    if (k < 0) return;  // the first RING steps only request pages
+    const bool full = p >= tile.fp0 && p < tile.fp1;
+    const int pos0 = p * kPage + 4 * lc;
+    bool vis[4] = {true, true, true, true};
+    uint32_t tokmask = 0xffffu;
+    if (!full) {
+      tokmask = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        vis[i] = col.on && pos0 + i >= col_lo && pos0 + i <= col_hi;
+        const uint64_t bal = __ballot(vis[i]);
+#pragma unroll
+        for (int g = 0; g < 4; ++g)
+          if ((bal >> (16 * g)) & 0xffffull) tokmask |= 1u << (4 * g + i);
+      }
+    }
+    if (k >= nk) tokmask = 0;  // past the last page
+    if (tokmask == 0) return;  // no column sees this page (or no page)
+    // partial scores over this wave's slice
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int j = 0; j < KS; ++j) sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[j], qop[j], sc, 0, 0, 0);
+    // stage this wave's V slice (tokens no column sees are zeroed: they may
+    // hold NaN)
+#pragma unroll
+    for (int j = 0; j < VL; ++j) {
+      const int e = (j * 64 + lane) * 8;
+      const int tok = e / HS;
+      u32x4 v = vr[j];
+      if (!full && !((tokmask >> tok) & 1u)) v = u32x4{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4 *>(vt + tok * VSTR + (e - tok * HS)) = v;
+    }
+    // whole scores: the 4 slices added in wave order, the same in every wave
+    f32x4 *xp = xs[xpar][0];
+    xpar ^= 1;
+    xp[wave * 64 + lane] = sc;
+    lds_barrier();
+    sc = xp[lane];
+#pragma unroll
+    for (int w = 1; w < kWaves; ++w) sc += xp[w * 64 + lane];
+
+    float sv[4];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      sv[i] = vis[i] ? sc[i] : -INFINITY;
+      mx = fmaxf(mx, sv[i]);
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float m2 = mx * kLog2e;
+    const bool grow = m2 > m_run + SLACK;
+    if (__ballot(grow) != 0) {
+      const float m_new = grow ? m2 : m_run;
+      const float alpha = grow ? fast_exp2(m_run - m_new) : 1.f;
+      m_run = m_new;
+      if (lc == 0) xfer[wave][ln] = alpha;
+      wave_lds_sync();
+      const f32x4 al = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+#pragma unroll
+      for (int u = 0; u < DS; ++u) oacc[u] *= al;
+      lacc *= al;
+    }
+    float pr[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      pr[i] = fast_exp2(__builtin_fmaf(sv[i], kLog2e, -m_run));
+      if (!full) pr[i] = sv[i] == -INFINITY ? 0.f : pr[i];
+    }
+    const s16x4 pa = pack_weights(pr[0], pr[1], pr[2], pr[3]);
+    wave_lds_sync();  // the staged V slice is visible to the whole wave
+#pragma unroll
+    for (int u = 0; u < DS; ++u) {
+      const s16x4 vb = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+          (__attribute__((address_space(3))) s16x4 *)(vtr + 16 * u));
+      oacc[u] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, vb, oacc[u], 0, 0, 0);
+    }
+    lacc = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pa, ones, lacc, 0, 0, 0);
+    wave_lds_sync();  // the V slice's reads are done before the next page stages its own
+  };
+
+  if (nk > 0) {
+    fetch_window(0);
+    bf16x8 kset[RING + 1][KS];
+    u32x4 vset[RING + 1][VL];
+    // The loop starts RING steps early: those steps only request pages 0 ..
+    // RING - 1, through the same code as every later refill (a separate
+    // prologue would be scheduled differently, and the compiler would then
+    // wait as if its last loads were the ones still in flight).  Step k uses
+    // set (k + RING) mod (RING + 1) and refills the set of step k - 1.
+    for (int k = -RING; k < nk; k += RING + 1) {
+#pragma unroll
+      for (int r = 0; r <= RING; ++r) page(k + r, kset[r], vset[r], kset[(r + RING) % (RING + 1)], vset[(r + RING) % (RING + 1)]);
+    }
+  }
+  wait_all_memory();
+
+  // ---- results: every wave holds the same (m, l) and its own hd slice ----
+  if (lc == 0) xfer[wave][ln] = m_run;
+  wave_lds_sync();
+  const f32x4 mo = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
+  const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
+  const bool fused = a.splits > 1 && a.counters != nullptr;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * lc + i;
+    if (r >= ncols) continue;
+    const Column rc = tile_column(r, a.group, nrows, hb, 16);
+    const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+    if (a.splits == 1) {
+      const float l = lacc[i];
+#pragma unroll
+      for (int u = 0; u < DS; ++u) {
+        const float v = l > 0.f ? oacc[u][i] / l : 0.f;
+        a.out[th * HD + h0 + 16 * u + ln] = f32_to_bf16_rne(v);
+      }
+    } else {
+      const int64_t ps = th * a.splits + split;
+      float *po = a.part_o + ps * HD + h0;
+#pragma unroll
+      for (int u = 0; u < DS; ++u) store_coherent(po + 16 * u + ln, oacc[u][i]);
+      if (wave == 0 && ln == 0) {
+        store_coherent(a.part_ml + 2 * ps, mo[i]);
+        store_coherent(a.part_ml + 2 * ps + 1, lacc[i]);
+      }
+    }
+  }
+  if (!fused) return;
+  __syncthreads();  // the V staging area is free for the merge scratch
+  if (a.spin_ticks > 0) {
+    owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, &s_is_last);
+    return;
+  }
+  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]),
+                            &s_is_last);
 }
 
-// Separate merge: one workgroup per (row, query head, 32 hd elements).
-__global__ __launch_bounds__(kThreads) void pgqa_combine_kernel(DecodeArgs a, int hd) {
-  __shared__ ChunkScratch cs;
+// ---- merge of one block of 32 consecutive hd elements of one (row, query head) ----
+// The per-element arithmetic: M = max m_s over the non-empty splits
+// (l_s > 0), w_s = exp2(m_s - M) (0 for an empty split); for each of the 8
+// split groups g (split s is in group s mod 8) an fma chain over the group's
+// splits in increasing order gives num_g = sum w_s o_s[d] and
+// den_g = sum w_s l_s; out = (num_0 + ... + num_7) / (den_0 + ... + den_7),
+// the sums taken in group order (0 if the denominator is 0).  The combine
+// kernel and both forms of the fused merge run exactly this, so their bits
+// agree.
+// One wave merges a block: lane l takes split group l / 8 and elements
+// 4 (l mod 8) .. 4 (l mod 8) + 3.  It loads the (m, l) and the 4 partial
+// elements of every split of its group (16-byte loads, all issued before any
+// is used: one memory round trip, two past 128 splits), and the block max,
+// the group denominators and the group sums are exchanged between lanes: no
+// LDS, no barrier.  CPOL is the loads' cache policy: plain after a kernel
+// boundary, device-coherent (read past this XCD's L2) inside the decode
+// launch.  `live` false: nothing is loaded or written.
+constexpr int kCpolPlain = 0;
+constexpr int kCpolDevice = 16;           // sc1
+constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer
+constexpr int kMergeBatch = 16;           // splits per group per round trip
+template <int CPOL>
+__device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, bool live) {
+  if (!live) return;
+  const int g = lane >> 3, q = lane & 7;
+  const int S = a.splits;
+  const int ni = (S + kMergeGroups - 1) / kMergeGroups;  // splits per group (at most)
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + th * S * hd, 0, S * hd * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(a.part_ml + th * S * 2, 0, S * 8, kBufferWord3);
+  // (m, l) of the group's splits: the group's i-th split (s = g + 8 i) is
+  // loaded by lane 8 g + (i mod 8), as its (i / 8)-th pair (past split S - 1:
+  // split S - 1 again, never used)
+  constexpr int kPairs = kMaxSplits / kMergeGroups / 8;  // pairs per lane
+  f32x2 mlk[kPairs];
+  float mx = -INFINITY;
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int i = q + 8 * k;
+    mlk[k] = f32x2{0.f, 0.f};
+    if (8 * k < ni) {
+      mlk[k] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(
+                                             rml, min(g + kMergeGroups * i, S - 1) * 8, 0, CPOL));
+    }
+  }
+  f32x4 v[kMergeBatch];
+  auto load_batch = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i)
+      if (i0 + i < ni)
+        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                             ro, (min(g + kMergeGroups * (i0 + i), S - 1) * hd + d0 + 4 * q) * 4, 0,
+                                             CPOL));
+  };
+  load_batch(0);
+#pragma unroll
+  for (int k = 0; k < kPairs; ++k) {
+    const int i = q + 8 * k;
+    if (i < ni && g + kMergeGroups * i < S && mlk[k].y > 0.f) mx = fmaxf(mx, mlk[k].x);
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+  float dg = 0.f;
+  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  const int lead = lane & ~7;  // lane 8 g
+  auto chain = [&](int i0) __attribute__((always_inline)) {
+#pragma unroll
+    for (int i = 0; i < kMergeBatch; ++i) {
+      const int ii = i0 + i;
+      if (ii < ni) {
+        const float m_s = __shfl(mlk[ii >> 3].x, lead + (ii & 7));
+        const float l_s = __shfl(mlk[ii >> 3].y, lead + (ii & 7));
+        if (g + kMergeGroups * ii < S) {
+          const float ws = l_s > 0.f ? fast_exp2(m_s - mx) : 0.f;
+          if (ws != 0.f) {
+            dg = __builtin_fmaf(ws, l_s, dg);
+#pragma unroll
+            for (int c = 0; c < 4; ++c) num[c] = __builtin_fmaf(ws, v[i][c], num[c]);
+          }
+        }
+      }
+    }
+  };
+  chain(0);
+  if (ni > kMergeBatch) {  // more than 128 splits: a second round trip
+    load_batch(kMergeBatch);
+    chain(kMergeBatch);
+  }
+  // sums over the 8 groups in group order
+  float den = 0.f;
+  f32x4 n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int gg = 0; gg < kMergeGroups; ++gg) {
+    den += __shfl(dg, gg * 8);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] += __shfl(num[c], gg * 8 + q);
+  }
+  if (g == 0) {
+    uint16_t *op = a.out + th * hd + d0 + 4 * q;
+#pragma unroll
+    for (int c = 0; c < 4; ++c) op[c] = f32_to_bf16_rne(den > 0.f ? n[c] / den : 0.f);
+  }
+}
+
+// Separate merge: one wave per (row, query head, 32 hd elements).
+__global__ __launch_bounds__(64) void pgqa_combine_kernel(DecodeArgs a, int hd) {
   const int chunks = hd / 32;
   const int64_t th = blockIdx.x / chunks;
   const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
-  merge_chunk32(a, LoadPlain{}, th, d0, hd, threadIdx.x, true, cs);
+  merge_wave32<kCpolPlain>(a, th, d0, hd, threadIdx.x, true);
 }
 
-// ---- parallel fused merge of one unit (claimed slices) ----
-// The unit's counter word holds arrivals and claims in its low 16 bits and
-// finished slices in its high 16 bits.
-//  1. Every workgroup (partials written through and complete) adds 1: the
-//     workgroup that draws S - 1 is the last to arrive.
-//  2. The others wait for the count to reach S, at most spin_ticks of the
-//     100 MHz real-time counter (or until they see the count below their own
-//     arrival: the unit is merged already); one that gives up leaves without
-//     touching the word again.
-//  3. Every workgroup still present claims slices -- pairs of 32-element
-//     output chunks of the unit -- with fetch-and-add on the low bits
-//     (slice = old count - S) and merges each with the combine kernel's
-//     per-element code.  A claim past the last slice (or after the reset) is
-//     taken back with a subtraction.  The last arrival claims until none are
-//     left, so every slice is merged even if all the others gave up.
-//  4. Each merged slice adds 1 << 16; the workgroup that completes the last
-//     slice subtracts what arrivals, claims and completions added (S +
-//     nslices + (nslices << 16)); claims taken back net to zero, so the word
-//     is zero again for the next call.
+// ---- parallel fused merge of one unit (owned blocks) ----
+// The unit's outputs are cut into blocks of 32 elements; block b belongs to
+// the workgroup of split b mod S, whose waves merge its blocks one each.  Three counter words per
+// unit, on separate cache lines: arrivals, a ready flag and a done count.
+//  1. Every workgroup, once its partial stores have completed (they write
+//     through to memory), adds 1 to the arrival word.  The one that draws
+//     S - 1 is the last to arrive: every partial of the unit is in memory,
+//     and it sets the ready flag.
+//  2. A workgroup that owns blocks polls the flag -- a word written once,
+//     so polling it does not slow the arrivals down -- for at most
+//     spin_ticks of the 100 MHz real-time counter, then merges its blocks
+//     with the combine kernel's per-element arithmetic (device-coherent
+//     loads).  One that gives up merges nothing.
+//  3. Every workgroup adds 1 + (blocks merged << 16) to the done word.  The
+//     one that completes it (low half S - 1) is the last to touch any of the
+//     three words: if fewer than all blocks were merged (a workgroup gave up),
+//     it merges every block itself -- merging a block twice writes the same
+//     bits -- and then it resets the three words to zero for the next call.
 // No workgroup waits on another for more than spin_ticks, and none needs
 // another to be resident: a launch larger than the device holds only merges
-// with fewer helpers.
-constexpr int64_t kParallelMergeBytes = int64_t(2) << 20;  // per-unit partials from which the merge goes parallel
-constexpr int kClaimSpinTicks = 2000;                      // 20 us
+// later.
+constexpr int64_t kParallelMergeBytes = int64_t(256) << 10;  // per-unit partials from which the merge goes parallel
+constexpr int kClaimSpinTicks = 2000;                        // 20 us
+constexpr int kFlagBase = 2048;  // ready flags: counters[kFlagBase + unit]
+constexpr int kDoneBase = 3072;  // done counts: counters[kDoneBase + unit]
+constexpr int kOwnedMergeUnits = 1024;  // units the three-word layout holds
 // Bound of the parallel merge's waits for the calls that follow, set by
 // pgqa_set_merge_wait_ticks (0: kClaimSpinTicks).
 std::atomic<int> g_merge_wait_ticks{0};
 
-// One claimed slice: chunks 2 slice and 2 slice + 1 of the unit's outputs,
-// one per 256-thread half (a 256-thread workgroup merges them one after the
-// other, with the same per-element steps).
+// Blocks first, first + step, ... below nblocks of the unit (block b: column
+// b / (HD / 32), elements (b mod (HD / 32)) 32 ..), taken by the workgroup's
+// waves in turn.  Returns how many blocks this workgroup merged (the same in
+// every thread).
 template <int HD, int NT>
-__device__ __forceinline__ void merge_slice(const DecodeArgs &a, int t0, int kh, int hb, int nrows,
-                                                      int nchunks, int cap, int slice, ChunkScratch *cs) {
+__device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int nblocks, int cap, int first,
+                            int step) {
   constexpr int per_col = HD / 32;
-  const int tid = threadIdx.x;
-  const int half0 = NT == kThreads ? 0 : tid >> 8;
-#pragma unroll
-  for (int half = half0; half < (NT == kThreads ? 2 : half0 + 1); ++half) {
-    const int c = 2 * slice + half;
-    const bool live = c < nchunks;
-    const int cc = live ? c : 2 * slice;
-    const Column rc = tile_column(cc / per_col, a.group, nrows, hb, cap);
+  constexpr int waves = NT / 64;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  for (int b = first + wave * step; b < nblocks; b += waves * step) {
+    const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
     const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-    merge_chunk32(a, LoadCoherent{}, th, (cc % per_col) * 32, HD, tid & 255, live, cs[NT == kThreads ? 0 : half]);
+    merge_wave32<kCpolDevice>(a, th, (b % per_col) * 32, HD, lane, true);
   }
+  return first < nblocks ? (nblocks - first + step - 1) / step : 0;
 }
 
 template <int HD, int NT>
-__device__ void claimed_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
-                              ChunkScratch *cs, int *s_word) {
-  static_assert(NT == kThreads || NT == 2 * kThreads, "a claim is two chunks: one per 256 threads, or both in turn");
-  int32_t *w = a.counters + (t0 * a.nkv + kh) * a.hblocks + hb;
+__device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
+                            int *s_word) {
+  const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
+  int32_t *arrive = a.counters + unit;
+  int32_t *flag = a.counters + kFlagBase + unit;
+  int32_t *done = a.counters + kDoneBase + unit;
   const int S = a.splits;
-  const int nchunks = ncols * (HD / 32);
-  const int nslices = (nchunks + 1) / 2;
+  const int nblocks = ncols * (HD / 32);
   const int tid = threadIdx.x;
   wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
   if (tid == 0) {
-    const int t = __hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
+    const int t = __hip_atomic_fetch_add(arrive, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     bool ready = t == S - 1;
-    if (!ready) {
+    if (ready) {
+      __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    } else if (split < nblocks) {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
-      while (!ready && __builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(a.spin_ticks)) {
-        __builtin_amdgcn_s_sleep(20);  // ~1300 clocks: a few hundred waiters poll one word
-        const int low = __hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff;
-        if (low <= t) break;
-        ready = low >= S;
+      while (__builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(a.spin_ticks)) {
+        if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
+          ready = true;
+          break;
+        }
+        __builtin_amdgcn_s_sleep(2);
       }
     }
     *s_word = ready;
   }
   __syncthreads();
-  if (!*s_word) return;
-  for (;;) {
-    __syncthreads();  // everyone has read the previous claim
+  // pass 0: this workgroup's own blocks (if it saw the flag); pass 1, only in
+  // the last workgroup to finish and only if some workgroup gave up: every
+  // block (a block merged twice gets the same bits).  One call site keeps
+  // the merge code in the kernel once.
+  int first = split, step = S;
+  for (int pass = 0; pass < 2; ++pass) {
+    int merged = 0;
+    if (*s_word > 0) merged = merge_blocks<HD, NT>(a, t0, kh, hb, nrows, nblocks, cap, first, step);
+    __syncthreads();  // every thread has read s_word
+    if (pass == 1) break;
     if (tid == 0) {
-      // look first: once every slice is claimed (or the word is reset) no
-      // atomic is needed to learn it
-      const int seen = (__hip_atomic_load(w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff) - S;
-      int slice = -1;
-      if (seen >= 0 && seen < nslices) {
-        slice = (__hip_atomic_fetch_add(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) & 0xffff) - S;
-        if (slice < 0 || slice >= nslices) {
-          __hip_atomic_fetch_sub(w, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          slice = -1;
-        }
-      }
-      *s_word = slice;
+      const int d = __hip_atomic_fetch_add(done, 1 + (merged << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      *s_word = (d & 0xffff) != S - 1 ? -1 : ((d >> 16) + merged < nblocks ? 1 : 0);
     }
     __syncthreads();
-    const int slice = *s_word;
-    if (slice < 0) return;
-    merge_slice<HD, NT>(a, t0, kh, hb, nrows, nchunks, cap, slice, cs);
-    __syncthreads();
-    if (tid == 0) {
-      const int done = __hip_atomic_fetch_add(w, 1 << 16, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) >> 16;
-      if (done == nslices - 1)
-        __hip_atomic_fetch_sub(w, S + nslices + (nslices << 16), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
+    if (*s_word < 0) return;  // not the last to finish
+    first = 0;
+    step = 1;
+  }
+  // the last workgroup to finish: nobody touches the three words any more
+  if (tid == 0) {
+    __hip_atomic_store(arrive, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
 }
 
@@ -1037,7 +1375,6 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   __shared__ int s_is_last;
   __shared__ int3 s_tiles[64];  // tiles whose parallel merge follows the page loop (row, rows, columns)
   static_assert(sizeof(FusedScratch<kSharedThreads>) <= sizeof(slot0), "merge scratch must fit a ring slot");
-  static_assert(2 * sizeof(ChunkScratch) <= sizeof(slot0), "chunk merge scratch must fit a ring slot");
   static_assert(256 * MCH * 16 <= sizeof(slot0), "team merge round must fit a ring slot");
   // Ring slot I as a direct reference to its own object (no pointer table):
   // the compiler then knows which object every LDS access touches.
@@ -1415,8 +1752,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   for (int i = 0; i < n_tiles; ++i) {
     const int3 tl = s_tiles[i];
     const int ncols_i = tl.z;
-    claimed_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, ncols_i, CAP, reinterpret_cast<ChunkScratch *>(slot0),
-                                      &s_is_last);
+    owned_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, ncols_i, CAP, split, &s_is_last);
     __syncthreads();
   }
 }
@@ -1424,26 +1760,23 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
 
 using pgqa_detail::fail;
 
-// Which kernel runs and how rows are tiled, from the call's shapes and split
-// count only (so calls that differ only in data -- merge mode, page placement
-// -- run the same code).  The shared-page kernel takes, from hd 128 up, tiles
-// of more than 16 columns (groups of 8 or more; every group at hd 512); the
-// per-wave kernel the rest.  At hd 512 the per-wave kernel takes tiles of up
-// to 16 columns from 64 splits up (long spans, bandwidth-bound): its 4 waves
-// each keep a whole 32 KB K/V page in flight, twice what the shared-page
-// kernel's two-slot ring holds at hd 512, and from there on a fused merge is
-// always the parallel one.  Shorter hd-512 calls are latency-bound and stay on
-// the shared-page kernel.  With fewer columns than the shared-page kernel's
-// 64 the hd is cut into slices so that all 4 waves still have work.
+// Which kernel runs and how rows are tiled, from the call's shapes only (so
+// calls that differ only in data -- merge mode, page placement -- run the same
+// code).  The shared-page kernel takes, from hd 128 up, tiles of more than 16
+// columns (groups of 8 or more; every group at hd 512); hd-512 tiles of up to
+// 16 columns go to the hd-sliced kernel (measured against the per-wave kernel
+// at hd 512: 28.3 against 31.8 us of kernel time on a 32K-key, 8-column call,
+// and faster from 11 to 256 splits); the per-wave kernel takes the rest.
+// With fewer columns than the shared-page kernel's 64 the hd is cut into
+// slices so that all 4 waves still have work.
 struct Plan {
-  int kind;     // 0: per-wave kernel, 1: shared-page kernel
+  int kind;     // 0: per-wave kernel, 1: shared-page kernel, 2: hd-sliced kernel
   int wide = 0; // shared-page kernel with the teams on separate columns (prefill)
   int nsl;      // hd slices per column block (shared-page kernel)
   int cap;      // columns per tile
   int rmax;     // rows per tile
   int hblocks;  // head blocks per kv head
 };
-constexpr int64_t kWave512MinSplits = 64;
 Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   Plan p;
   const int64_t cols = group <= 64 ? group * (rows < 64 / group ? rows : 64 / group) : 64;
@@ -1451,7 +1784,8 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   // (multi-row decode); narrower groups keep the per-wave kernel, whose
   // 16-column tiles waste nothing when every row has its own sequence
   p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) ? 1 : 0;
-  if (hd == 512 && splits < kWave512MinSplits) p.kind = 1;
+  // hd-512 tiles of up to 16 columns: the hd-sliced kernel
+  if (hd == 512 && cols <= 16) p.kind = 2;
   p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
   if (p.kind == 1 && hd == 128 && p.nsl == 4) p.nsl = 2;  // hd 128 has 4 QK steps
   if (p.kind == 1 && hd == 512 && p.nsl == 1) p.nsl = 2;  // a whole hd-512 slice needs too many registers
@@ -1509,7 +1843,13 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
       return hipErrorInvalidValue;
     }
   }
-  hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
+  if constexpr (HD == 512) {
+    // every hd-512 plan is the shared-page or the hd-sliced kernel
+    if (p.kind != 2) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(pgqa_slice_kernel<HD>, grid, block, 0, stream, a);
+  } else {
+    hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
+  }
   return hipGetLastError();
 }
 
@@ -1596,7 +1936,7 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
   const int64_t combine_blocks = rows * nh * (hd / 32);
-  if (splits > 1 && !counters && combine_blocks * kThreads > int64_t(UINT32_MAX))
+  if (splits > 1 && !counters && combine_blocks * 64 > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "combine grid of %lld workgroups too large", (long long)combine_blocks);
 
   DecodeArgs a;
@@ -1629,14 +1969,16 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   // start; it pays only when the launch is larger than what the GPU holds at
   // once (2-3 per-wave workgroups per CU), so that the order of dispatch
   // decides how the launch ends.
-  a.rank_rows = plan.kind == 0 && rows > 1 && blocks > kRankMinBlocks;
+  a.rank_rows = plan.kind != 1 && rows > 1 && blocks > kRankMinBlocks;
 
   // The merge of one unit reads splits * cap * hd floats of partials: from
-  // 2 MB up the unit's workgroups merge it together (shared-page kernel, and
-  // the per-wave kernel from hd 256), below that the last one to arrive
-  // merges it alone.
+  // 256 KB up the unit's workgroups merge it together, each its own blocks
+  // (every kernel from hd 256, the shared-page kernel from hd 128; at most
+  // kOwnedMergeUnits units, the counter layout of that merge), below that the
+  // last one to arrive merges it alone.  Both give the same bits.
   const int wait_ticks = g_merge_wait_ticks.load(std::memory_order_relaxed);
-  a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind == 1 || hd >= 256) &&
+  a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind != 0 || hd >= 256) &&
+                         rows * nkv * plan.hblocks <= kOwnedMergeUnits &&
                          splits * plan.cap * hd * 4 >= kParallelMergeBytes
                      ? (wait_ticks > 0 ? wait_ticks : kClaimSpinTicks)
                      : 0;
@@ -1650,8 +1992,8 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   }
   if (err != hipSuccess) return fail(PGQA_ELAUNCH, "split kernel launch: %s", hipGetErrorString(err));
   if (splits > 1 && !counters) {
-    hipLaunchKernelGGL(pgqa_combine_kernel, dim3(static_cast<unsigned>(rows * nh * (hd / 32))), dim3(kThreads), 0, st,
-                       a, static_cast<int>(hd));
+    hipLaunchKernelGGL(pgqa_combine_kernel, dim3(static_cast<unsigned>(rows * nh * (hd / 32))), dim3(64), 0, st, a,
+                       static_cast<int>(hd));
     err = hipGetLastError();
     if (err != hipSuccess) return fail(PGQA_ELAUNCH, "combine kernel launch: %s", hipGetErrorString(err));
   }
