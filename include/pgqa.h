@@ -136,6 +136,34 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool,
                      int64_t hd, int64_t window, int64_t splits, int32_t *counters,
                      const int32_t *page_map, void *stream);
 
+/* Bytes of partial results pgqa_attn_decode_noalloc can hold: 32 MiB. */
+#define PGQA_NOALLOC_SCRATCH_BYTES (32u << 20)
+
+/*
+ * pgqa_attn_decode without the caller's partial buffer and counters, for
+ * callers that cannot allocate device memory (code under HIP graph capture,
+ * tight serving loops, harnesses that forbid allocation).  It allocates
+ * nothing: the split partials live in a static device array of
+ * PGQA_NOALLOC_SCRATCH_BYTES that the library holds on each GPU it runs on
+ * until the process ends (its address is looked up once per device, with
+ * that device current; no hipMalloc, hipFree or allocating library call),
+ * and the splits are merged by the separate combine kernel.
+ * Arguments, computation, rounding and return codes: as pgqa_attn_decode with
+ * part = the scratch and counters = NULL, so the result is bit for bit that
+ * call's for the same split count.  In addition it returns PGQA_EINVAL when
+ * splits > 1 and rows * nh * splits * (hd + 2) * 4 exceeds
+ * PGQA_NOALLOC_SCRATCH_BYTES (use fewer splits or pgqa_attn_decode), and
+ * PGQA_ELAUNCH when the scratch address cannot be had.
+ * Every call on one GPU uses that GPU's one scratch array, which keeps the
+ * last call's contents (nothing in it needs to start at zero): calls that
+ * overlap on one GPU (concurrent streams, other threads) race and must not
+ * happen.
+ */
+int pgqa_attn_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                             const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
+                             const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
+                             int64_t window, int64_t splits, const int32_t *page_map, void *stream);
+
 /*
  * Rows per prefill tile (span-02 test page, `run()`, the prefill section: the
  * `prefill_rows_per_tile(hd)` argument of `make_tiles`).  64 for every

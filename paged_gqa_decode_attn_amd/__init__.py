@@ -9,8 +9,9 @@ CPU or framework fallback, and a missing library is an error.
 Entry points (same names and argument order as the C ABI, after the span-02
 GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
 ``counter_capacity``, ``attn_decode``, ``prefill_rows_per_tile``,
-``make_tiles``, ``attn_prefill``; and ``qk_rope_prep``, the QK-norm + RoPE
-step that fills the pool before decode.
+``make_tiles``, ``attn_prefill``; ``qk_rope_prep``, the QK-norm + RoPE step
+that fills the pool before decode; ``attn_decode_noalloc``, decode for
+callers that cannot allocate; ``set_merge_wait_ticks``, a test hook.
 """
 from __future__ import annotations
 
@@ -60,6 +61,8 @@ def lib() -> ctypes.CDLL:
         h.pgqa_make_tiles.argtypes = [p, i64, i64, p, p, i64]
         h.pgqa_attn_prefill.restype = ctypes.c_int
         h.pgqa_attn_prefill.argtypes = [p, p, p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
+        h.pgqa_attn_decode_noalloc.restype = ctypes.c_int
+        h.pgqa_attn_decode_noalloc.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
         h.pgqa_set_merge_wait_ticks.restype = ctypes.c_int32
         h.pgqa_set_merge_wait_ticks.argtypes = [ctypes.c_int32]
         h.pgqa_qk_rope_prep.restype = ctypes.c_int
@@ -151,6 +154,41 @@ def attn_decode(out, part, q, k_pool, v_pool, block_table, page_origin, qpos, kv
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
     rc = lib().pgqa_attn_decode(*args, rows, nh, nkv, hd, window, splits, cnt, pm, stream)
+    if rc != OK:
+        raise PgqaError(rc, last_error())
+
+
+NOALLOC_SCRATCH_BYTES = 32 << 20
+
+
+def attn_decode_noalloc(out, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last,
+                        rows: int, nh: int, nkv: int, hd: int, window: int, splits: int,
+                        page_map=None, stream=None) -> None:
+    """Enqueue one decode call that allocates nothing (see
+    ``pgqa_attn_decode_noalloc`` in include/pgqa.h): partials in the library's
+    static device scratch, merged by the separate combine kernel.  Tensors as
+    for ``attn_decode``."""
+    import torch
+
+    b16 = (torch.bfloat16, torch.int16, torch.uint16)
+    i32 = (torch.int32,)
+    n_out = rows * nh * hd
+    args = [
+        _addr(out, "out", b16, n_out),
+        _addr(q, "q", b16, n_out),
+        _addr(k_pool, "k_pool", b16),
+        _addr(v_pool, "v_pool", b16),
+        _addr(block_table, "block_table", i32),
+        _addr(page_origin, "page_origin", i32, rows),
+        _addr(qpos, "qpos", i32, rows),
+        _addr(kv_last, "kv_last", i32, rows),
+    ]
+    pm = _addr(page_map, "page_map", i32)
+    if stream is None:
+        stream = torch.cuda.current_stream(out.device if hasattr(out, "device") else None).cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    rc = lib().pgqa_attn_decode_noalloc(*args, rows, nh, nkv, hd, window, splits, pm, stream)
     if rc != OK:
         raise PgqaError(rc, last_error())
 

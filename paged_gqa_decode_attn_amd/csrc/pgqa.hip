@@ -57,6 +57,11 @@
 #include "errors.h"
 #include "pgqa.h"
 
+// Bytes of the allocation-free entry point's partial-result scratch, and the
+// scratch itself (see noalloc_scratch).
+constexpr uint64_t kNoAllocScratchBytes = uint64_t(PGQA_NOALLOC_SCRATCH_BYTES);
+static __device__ __align__(256) uint8_t scratch[kNoAllocScratchBytes];
+
 namespace pgqa_detail {
 namespace {
 thread_local char g_error[512] = "";
@@ -1853,56 +1858,43 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
   return hipGetLastError();
 }
 
-}  // namespace
+// ---- the allocation-free entry point's scratch ----
+// Partials of pgqa_attn_decode_noalloc live in the file-scope array `scratch`
+// (below, outside this namespace); each GPU the library runs on holds its own
+// copy until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device memory: the device address of this GPU's copy is
+// taken once per device with hipGetSymbolAddress (device current) and kept in
+// `g_noalloc_ptr`; only that address is ever passed to a kernel.
+constexpr int kMaxDevices = 64;
+std::atomic<void *> g_noalloc_ptr[kMaxDevices];
 
-extern "C" {
-
-int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t rows_per_seq) {
-  if (kv_span < 1 || rows < 1 || nkv < 1) return 1;
-  if (rows_per_seq < 1 || rows_per_seq > rows) rows_per_seq = rows;
-  const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
-  const int64_t units = nseq * nkv;
-  const int64_t pages = (kv_span + kPage - 1) / kPage;
-  // Two regimes, measured over split counts 1..256 on every configuration
-  // and on sweeps of further lengths, head layouts and batch sizes:
-  //  - long spans are bandwidth-bound.  One sequence: about one workgroup per
-  //    CU on the 256 CUs (each workgroup's prologue and epilogue then come
-  //    once), at least 8 pages per split.  A batch: about 6 workgroups per CU
-  //    (with the longest rows dispatched first, uneven lengths still balance),
-  //    at most 16 splits, at least 16 pages per split;
-  //  - short spans are latency-bound: about 64 workgroups in all, at least 4
-  //    pages per split.
-  // The larger of the two wins.
-  auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
-  const int64_t s_long = nseq == 1 ? std::min(cdiv(256, units), pages / 8)
-                                   : std::min(std::min(cdiv(1536, units), int64_t(16)), pages / 16);
-  const int64_t s_short = std::min(cdiv(64, units), pages / 4);
-  int64_t s = std::max(s_long, s_short);
-  if (s > kMaxSplits) s = kMaxSplits;
-  if (s < 1) s = 1;
-  return static_cast<int32_t>(s);
+// This device's scratch address, looked up on its first use (nullptr, with
+// the runtime's error in *err, if it cannot be had).
+void *noalloc_scratch(int *err) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+    *err = e != hipSuccess ? static_cast<int>(e) : static_cast<int>(hipErrorInvalidDevice);
+    return nullptr;
+  }
+  void *p = g_noalloc_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+  if (e != hipSuccess || !p) {
+    *err = static_cast<int>(e != hipSuccess ? e : hipErrorInvalidSymbol);
+    return nullptr;
+  }
+  g_noalloc_ptr[dev].store(p, std::memory_order_release);  // the same address whichever thread stores it
+  return p;
 }
 
-uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_t hd) {
-  if (rows < 1 || nh < 1 || splits < 1 || hd < 1) return 0;
-  return static_cast<uint64_t>(rows) * nh * splits * (hd + 2) * 4;
-}
-
-int32_t pgqa_counter_capacity(void) { return kCounterCap; }
-
-const char *pgqa_last_error(void) { return pgqa_detail::error_text(); }
-
-int32_t pgqa_set_merge_wait_ticks(int32_t ticks) {
-  if (ticks < 0) return PGQA_EINVAL;
-  return g_merge_wait_ticks.exchange(ticks, std::memory_order_relaxed);
-}
-
-int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,
-                     const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
-                     const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
-                     int64_t window, int64_t splits, int32_t *counters, const int32_t *page_map,
-                     void *stream) {
-  pgqa_detail::clear_error();
+// One decode call.  With `scratch_of` (the allocation-free entry point) the
+// partials go to this device's static scratch array instead of `part`, after
+// the shapes have been checked against its size.
+int decode_call(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,
+                const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos, const int32_t *kv_last,
+                int64_t rows, int64_t nh, int64_t nkv, int64_t hd, int64_t window, int64_t splits, int32_t *counters,
+                const int32_t *page_map, void *stream, void *(*scratch_of)(int *)) {
   if (!out || !q || !k_pool || !v_pool || !block_table || !page_origin || !qpos || !kv_last)
     return fail(PGQA_EINVAL, "a required pointer is NULL");
   if (rows < 1 || rows > INT_MAX / 2) return fail(PGQA_EINVAL, "rows=%lld out of range", (long long)rows);
@@ -1913,6 +1905,20 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
   if (window < 0 || window > INT_MAX) return fail(PGQA_EINVAL, "window=%lld out of range", (long long)window);
   if (splits < 1 || splits > kMaxSplits)
     return fail(PGQA_EINVAL, "splits=%lld outside 1..%d", (long long)splits, kMaxSplits);
+  if (scratch_of && splits > 1) {
+    // (hd + 2) * 4 >= 264 bytes per (row, head, split): the first test keeps
+    // the product below from overflowing
+    const bool too_big = static_cast<uint64_t>(rows) * nh * splits > kNoAllocScratchBytes / 264;
+    const uint64_t need = too_big ? 0 : static_cast<uint64_t>(rows) * nh * splits * (hd + 2) * 4;
+    if (too_big || need > kNoAllocScratchBytes)
+      return fail(PGQA_EINVAL,
+                  "partials of %llu bytes exceed the %llu-byte scratch of the allocation-free entry point "
+                  "(fewer splits, or pgqa_attn_decode with a partial buffer)",
+                  (unsigned long long)need, (unsigned long long)kNoAllocScratchBytes);
+    int err = 0;
+    part = scratch_of(&err);
+    if (!part) return fail(PGQA_ELAUNCH, "scratch address of this device: %s", hipGetErrorString((hipError_t)err));
+  }
   if (splits > 1 && !part) return fail(PGQA_EINVAL, "splits > 1 needs a partial buffer");
   if (part && (reinterpret_cast<uintptr_t>(part) & 3u)) return fail(PGQA_EINVAL, "partial buffer not 4-byte aligned");
   if ((reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k_pool) | reinterpret_cast<uintptr_t>(v_pool)) & 15u)
@@ -1998,6 +2004,69 @@ int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, c
     if (err != hipSuccess) return fail(PGQA_ELAUNCH, "combine kernel launch: %s", hipGetErrorString(err));
   }
   return PGQA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t rows_per_seq) {
+  if (kv_span < 1 || rows < 1 || nkv < 1) return 1;
+  if (rows_per_seq < 1 || rows_per_seq > rows) rows_per_seq = rows;
+  const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
+  const int64_t units = nseq * nkv;
+  const int64_t pages = (kv_span + kPage - 1) / kPage;
+  // Two regimes, measured over split counts 1..256 on every configuration
+  // and on sweeps of further lengths, head layouts and batch sizes:
+  //  - long spans are bandwidth-bound.  One sequence: about one workgroup per
+  //    CU on the 256 CUs (each workgroup's prologue and epilogue then come
+  //    once), at least 8 pages per split.  A batch: about 6 workgroups per CU
+  //    (with the longest rows dispatched first, uneven lengths still balance),
+  //    at most 16 splits, at least 16 pages per split;
+  //  - short spans are latency-bound: about 64 workgroups in all, at least 4
+  //    pages per split.
+  // The larger of the two wins.
+  auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+  const int64_t s_long = nseq == 1 ? std::min(cdiv(256, units), pages / 8)
+                                   : std::min(std::min(cdiv(1536, units), int64_t(16)), pages / 16);
+  const int64_t s_short = std::min(cdiv(64, units), pages / 4);
+  int64_t s = std::max(s_long, s_short);
+  if (s > kMaxSplits) s = kMaxSplits;
+  if (s < 1) s = 1;
+  return static_cast<int32_t>(s);
+}
+
+uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_t hd) {
+  if (rows < 1 || nh < 1 || splits < 1 || hd < 1) return 0;
+  return static_cast<uint64_t>(rows) * nh * splits * (hd + 2) * 4;
+}
+
+int32_t pgqa_counter_capacity(void) { return kCounterCap; }
+
+const char *pgqa_last_error(void) { return pgqa_detail::error_text(); }
+
+int32_t pgqa_set_merge_wait_ticks(int32_t ticks) {
+  if (ticks < 0) return PGQA_EINVAL;
+  return g_merge_wait_ticks.exchange(ticks, std::memory_order_relaxed);
+}
+
+int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,
+                     const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
+                     const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
+                     int64_t window, int64_t splits, int32_t *counters, const int32_t *page_map,
+                     void *stream) {
+  pgqa_detail::clear_error();
+  return decode_call(out, part, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last, rows, nh, nkv, hd, window,
+                     splits, counters, page_map, stream, nullptr);
+}
+
+int pgqa_attn_decode_noalloc(void *out, const void *q, const void *k_pool, const void *v_pool,
+                             const int32_t *block_table, const int32_t *page_origin, const int32_t *qpos,
+                             const int32_t *kv_last, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
+                             int64_t window, int64_t splits, const int32_t *page_map, void *stream) {
+  pgqa_detail::clear_error();
+  return decode_call(out, nullptr, q, k_pool, v_pool, block_table, page_origin, qpos, kv_last, rows, nh, nkv, hd,
+                     window, splits, nullptr, page_map, stream, &noalloc_scratch);
 }
 
 int32_t pgqa_prefill_rows_per_tile(int64_t hd) {

@@ -23,7 +23,8 @@ def test_library_exports_every_declared_symbol():
     names = declared_functions()
     assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
             "pgqa_counter_capacity", "pgqa_last_error", "pgqa_attn_prefill", "pgqa_make_tiles",
-            "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep", "pgqa_set_merge_wait_ticks"} <= set(names)
+            "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep", "pgqa_set_merge_wait_ticks",
+            "pgqa_attn_decode_noalloc"} <= set(names)
     h = ctypes.CDLL(pg.LIB_PATH)
     for n in names:
         assert getattr(h, n, None) is not None, n
@@ -135,6 +136,24 @@ def test_large_grids_that_fit_are_not_refused_for_their_size():
     error text only: refused before launch for another reason.)"""
     rc = call(rows=1 << 16, nh=64, nkv=64, hd=512, splits=2, cnt=FAKE)
     assert rc == pg.ECAP and "grid" not in pg.last_error()
+
+
+def test_noalloc_scratch_size_and_refusals():
+    """The allocation-free entry point refuses partials beyond its scratch
+    before it looks the scratch up (no HIP call), overflowing products
+    included; the Python constant is the header's."""
+    text = open(os.path.join(ROOT, "include", "pgqa.h")).read()
+    m = re.search(r"#define PGQA_NOALLOC_SCRATCH_BYTES \((\d+)u << (\d+)\)", text)
+    assert m and int(m.group(1)) << int(m.group(2)) == pg.NOALLOC_SCRATCH_BYTES
+    f = pg.lib().pgqa_attn_decode_noalloc
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p] * 8 + [ctypes.c_int64] * 6 + [ctypes.c_void_p] * 2
+    # 16 heads x 256 splits x hd 512 is 8.4 MB a row: 4 rows exceed 32 MiB
+    assert pg.decode_part_bytes(4, 16, 256, 512) > pg.NOALLOC_SCRATCH_BYTES
+    for rows, nh, nkv, hd, splits in ((4, 16, 2, 512, 256), ((1 << 30) - 1, 65536, 1, 512, 256)):
+        assert f(*[FAKE] * 8, rows, nh, nkv, hd, 0, splits, None, None) == pg.EINVAL
+        assert "scratch" in pg.last_error()
+    assert f(None, *[FAKE] * 7, 1, 4, 1, 64, 0, 2, None, None) == pg.EINVAL
 
 
 def test_merge_wait_ticks_hook():
