@@ -1114,8 +1114,9 @@ __global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
 // agree.
 // One wave merges a block: lane l takes split group l / 8 and elements
 // 4 (l mod 8) .. 4 (l mod 8) + 3.  It loads the (m, l) and the 4 partial
-// elements of every split of its group (16-byte loads, all issued before any
-// is used: one memory round trip, two past 128 splits), and the block max,
+// elements of every split of its group (16-byte loads, BATCH splits of each
+// group per memory round trip: one round trip for up to 8 BATCH splits, all
+// loads of a round issued before any is used), and the block max,
 // the group denominators and the group sums are exchanged between lanes: no
 // LDS, no barrier.  CPOL is the loads' cache policy: plain after a kernel
 // boundary, device-coherent (read past this XCD's L2) inside the decode
@@ -1123,8 +1124,10 @@ __global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
 constexpr int kCpolPlain = 0;
 constexpr int kCpolDevice = 16;           // sc1
 constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer
-constexpr int kMergeBatch = 16;           // splits per group per round trip
-template <int CPOL>
+// Splits per group per round trip: 16 (measured: 32, one round trip for
+// every S, is no faster in either merge and costs the combine 55 VGPRs).
+constexpr int kMergeBatch = 16;
+template <int CPOL, int BATCH>
 __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, bool live) {
   if (!live) return;
   const int g = lane >> 3, q = lane & 7;
@@ -1148,10 +1151,10 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
                                              rml, min(g + kMergeGroups * i, S - 1) * 8, 0, CPOL));
     }
   }
-  f32x4 v[kMergeBatch];
+  f32x4 v[BATCH];
   auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i)
+    for (int i = 0; i < BATCH; ++i)
       if (i0 + i < ni)
         v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
                                              ro, (min(g + kMergeGroups * (i0 + i), S - 1) * hd + d0 + 4 * q) * 4, 0,
@@ -1170,7 +1173,7 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
   const int lead = lane & ~7;  // lane 8 g
   auto chain = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
-    for (int i = 0; i < kMergeBatch; ++i) {
+    for (int i = 0; i < BATCH; ++i) {
       const int ii = i0 + i;
       if (ii < ni) {
         const float m_s = __shfl(mlk[ii >> 3].x, lead + (ii & 7));
@@ -1187,9 +1190,12 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
     }
   };
   chain(0);
-  if (ni > kMergeBatch) {  // more than 128 splits: a second round trip
-    load_batch(kMergeBatch);
-    chain(kMergeBatch);
+#pragma unroll
+  for (int i0 = BATCH; i0 < kMaxSplits / kMergeGroups; i0 += BATCH) {
+    if (ni > i0) {  // more than 8 i0 splits: another round trip
+      load_batch(i0);
+      chain(i0);
+    }
   }
   // sums over the 8 groups in group order
   float den = 0.f;
@@ -1212,18 +1218,23 @@ __global__ __launch_bounds__(64) void pgqa_combine_kernel(DecodeArgs a, int hd) 
   const int chunks = hd / 32;
   const int64_t th = blockIdx.x / chunks;
   const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
-  merge_wave32<kCpolPlain>(a, th, d0, hd, threadIdx.x, true);
+  merge_wave32<kCpolPlain, kMergeBatch>(a, th, d0, hd, threadIdx.x, true);
 }
 
 // ---- parallel fused merge of one unit (owned blocks) ----
-// The unit's outputs are cut into blocks of 32 elements; block b belongs to
-// the workgroup of split b mod S, whose waves merge its blocks one each.  Three counter words per
-// unit, on separate cache lines: arrivals, a ready flag and a done count.
+// The unit's outputs are cut into blocks of 32 elements and the blocks into
+// chunks of one block per wave of a workgroup; chunk c belongs to the
+// workgroup of split c mod S, whose waves merge its blocks one each.  Only
+// the workgroups of splits below the chunk count own a chunk.  The others
+// neither wait nor merge, so their done counts (step 3) land while the last
+// arrivals are still running instead of after the merge.  Three counter
+// words per unit, on separate cache lines: arrivals, a ready flag and a done
+// count.
 //  1. Every workgroup, once its partial stores have completed (they write
 //     through to memory), adds 1 to the arrival word.  The one that draws
 //     S - 1 is the last to arrive: every partial of the unit is in memory,
 //     and it sets the ready flag.
-//  2. A workgroup that owns blocks polls the flag -- a word written once,
+//  2. A workgroup that owns a chunk polls the flag -- a word written once,
 //     so polling it does not slow the arrivals down -- for at most
 //     spin_ticks of the 100 MHz real-time counter, then merges its blocks
 //     with the combine kernel's per-element arithmetic (device-coherent
@@ -1245,10 +1256,10 @@ constexpr int kOwnedMergeUnits = 1024;  // units the three-word layout holds
 // pgqa_set_merge_wait_ticks (0: kClaimSpinTicks).
 std::atomic<int> g_merge_wait_ticks{0};
 
-// Blocks first, first + step, ... below nblocks of the unit (block b: column
-// b / (HD / 32), elements (b mod (HD / 32)) 32 ..), taken by the workgroup's
-// waves in turn.  Returns how many blocks this workgroup merged (the same in
-// every thread).
+// Chunks first, first + step, ... of the unit (chunk c: blocks c * waves ..
+// c * waves + waves - 1 below nblocks, one per wave; block b: column
+// b / (HD / 32), elements (b mod (HD / 32)) 32 ..).  Returns how many blocks
+// this workgroup merged (the same in every thread).
 template <int HD, int NT>
 __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int nblocks, int cap, int first,
                             int step) {
@@ -1256,12 +1267,17 @@ __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nro
   constexpr int waves = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  for (int b = first + wave * step; b < nblocks; b += waves * step) {
-    const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
-    const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-    merge_wave32<kCpolDevice>(a, th, (b % per_col) * 32, HD, lane, true);
+  int merged = 0;
+  for (int c = first; c * waves < nblocks; c += step) {
+    const int b = c * waves + wave;
+    if (b < nblocks) {
+      const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
+      const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+      merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true);
+    }
+    merged += min(waves, nblocks - c * waves);
   }
-  return first < nblocks ? (nblocks - first + step - 1) / step : 0;
+  return merged;
 }
 
 template <int HD, int NT>
@@ -1273,6 +1289,7 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
   int32_t *done = a.counters + kDoneBase + unit;
   const int S = a.splits;
   const int nblocks = ncols * (HD / 32);
+  const int nchunks = (nblocks + NT / 64 - 1) / (NT / 64);
   const int tid = threadIdx.x;
   wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
@@ -1281,7 +1298,7 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
     bool ready = t == S - 1;
     if (ready) {
       __hip_atomic_store(flag, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    } else if (split < nblocks) {
+    } else if (split < nchunks) {
       const uint64_t t_start = __builtin_amdgcn_s_memrealtime();
       while (__builtin_amdgcn_s_memrealtime() - t_start < static_cast<uint64_t>(a.spin_ticks)) {
         if (__hip_atomic_load(flag, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != 0) {
