@@ -65,6 +65,19 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
  */
 uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_t hd);
 
+/*
+ * Splits that a tile of a decode call actually works on (ours; the pages
+ * leave the split of a row to the implementation).  A tile is a run of rows
+ * on one sequence that attn_decode processes together; `pages` is the number
+ * of KV pages its rows can see (the pages from the first visible key of any
+ * of its rows to the last).  Result: min(splits, ceil(pages / 16)), at least
+ * 1, with splits clamped to PGQA_MAX_SPLITS -- so every split of a tile
+ * covers at least 16 pages (or all of them).  Splits of the tile past that
+ * count do no work, and the merge reads only the partials of the others; a
+ * tile of one split is written without a merge.  Never fails.
+ */
+int32_t pgqa_tile_splits(int64_t pages, int64_t splits);
+
 /* Entries of int32 the merge-counter buffer must hold: 4096 (span-02 test page,
  * `run()`, the zeroed `cnt` buffer of 4096 * 4 bytes). */
 int32_t pgqa_counter_capacity(void);
@@ -98,7 +111,8 @@ int32_t pgqa_counter_capacity(void);
  *               kv_last == qpos is checked against its reference.
  *   rows, nh, nkv, hd  shapes: nh % nkv == 0, hd in {64, 128, 256, 512}
  *   window      0 = global causal, > 0 = sliding window of that many keys
- *   splits      1..PGQA_MAX_SPLITS, normally from pgqa_choose_splits
+ *   splits      1..PGQA_MAX_SPLITS, normally from pgqa_choose_splits; a tile
+ *               of rows works on pgqa_tile_splits(its pages, splits) of them
  *   counters    NULL: a separate combine kernel merges the splits.  Non-NULL:
  *               int32 [pgqa_counter_capacity()], all zero before the first
  *               call, and the merge happens inside the decode launch: the last
@@ -122,7 +136,8 @@ int32_t pgqa_counter_capacity(void);
  * and read each KV page once.  Bitwise properties, for a given split count:
  * the result does not depend on `counters` (fused merge == separate combine),
  * nor on where pages live in the pool (identity table == permuted pool behind
- * a page map).  Different split counts may differ in the last bits.
+ * a page map).  Different split counts may differ in the last bits (calls
+ * whose tiles all get the same pgqa_tile_splits counts give the same bits).
  * `out` must not alias any input or `part`.  Calls that share `part` or
  * `counters` must not run concurrently.
  * Returns PGQA_OK, PGQA_EINVAL (also for shapes whose launch grid would

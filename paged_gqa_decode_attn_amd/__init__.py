@@ -46,6 +46,8 @@ def lib() -> ctypes.CDLL:
         i64, p = ctypes.c_int64, ctypes.c_void_p
         h.pgqa_choose_splits.restype = ctypes.c_int32
         h.pgqa_choose_splits.argtypes = [i64, i64, i64, i64]
+        h.pgqa_tile_splits.restype = ctypes.c_int32
+        h.pgqa_tile_splits.argtypes = [i64, i64]
         h.pgqa_decode_part_bytes.restype = ctypes.c_uint64
         h.pgqa_decode_part_bytes.argtypes = [i64, i64, i64, i64]
         h.pgqa_counter_capacity.restype = ctypes.c_int32
@@ -73,6 +75,11 @@ def lib() -> ctypes.CDLL:
 
 def choose_splits(kv_span: int, rows: int, nkv: int, rows_per_seq: int) -> int:
     return int(lib().pgqa_choose_splits(kv_span, rows, nkv, rows_per_seq))
+
+
+def tile_splits(pages: int, splits: int) -> int:
+    """Splits a tile of ``pages`` visible KV pages works on (``pgqa_tile_splits``)."""
+    return int(lib().pgqa_tile_splits(pages, splits))
 
 
 def decode_part_bytes(rows: int, nh: int, splits: int, hd: int) -> int:

@@ -253,20 +253,19 @@ struct Tile {
 };
 // With force_rows > 0 (prefill) the tile is rows t0 .. t0 + force_rows - 1 as
 // the caller cut them, shortened to the run that shares row t0's origin.
-__device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane, int force_rows = 0) {
+// The tile from lane l's row t0 + l (lrow: that row exists and is within
+// the tile's span; org_l, qp_l, hi_l: its page origin, query position and
+// last visible key) and row t0 - 1's origin.
+__device__ __forceinline__ Tile tile_from(const DecodeArgs &a, int t0, int lane, int force_rows, bool lrow, int org_l,
+                                          int qp_l, int hi_l, int prev_origin) {
   Tile t;
-  const int span = force_rows > 0 ? force_rows : a.rmax;
-  const bool lrow = lane < span && t0 + lane < a.rows;
-  const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
-  const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
-  t.hi_l = lrow ? a.kv_last[t0 + lane] : -1;
+  t.hi_l = lrow ? hi_l : -1;
   t.origin = __builtin_amdgcn_readfirstlane(org_l);
   if (force_rows > 0) {
     t.lead = true;
     const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin));
     t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
   } else {
-    const int prev_origin = t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
     t.lead = t0 % a.rmax == 0 || prev_origin != t.origin;
     const uint64_t stop = __ballot(lane >= 1 && (!lrow || org_l != t.origin || (t0 + lane) % a.rmax == 0));
     t.nrows = stop ? static_cast<int>(__builtin_ctzll(stop)) : 64;
@@ -292,6 +291,86 @@ __device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane,
   t.fp0 = (lo_all + kPage - 1) / kPage;
   t.fp1 = hi_all >= lo_all ? (hi_all + 1) / kPage : t.fp0;
   return t;
+}
+
+// Launches of at most 64 rows that rank them (large launches, whose later
+// workgroups start while the earlier ones stream): every row's page origin,
+// query position and last visible key read once through the scalar cache,
+// into lane r = row r.  A workgroup that starts while the others stream K/V waits
+// behind their loads in the vector memory queue (measured on the batched
+// decode: 12-27 us per dependent round trip); scalar loads take another
+// path, and the tile is then built from these lanes without a second load.
+// Whole 16-row chunks are read with one wide load per array, the rest row
+// by row: nothing past row rows - 1 is read.
+struct LaneRows {
+  int org, qp, kl;
+};
+typedef const __attribute__((address_space(4))) int32_t ScalarInt;
+__device__ __forceinline__ LaneRows rows_by_lane(const DecodeArgs &a, int lane) {
+  LaneRows m{INT_MIN, 0, -1};
+  ScalarInt *po = (ScalarInt *)a.page_origin;
+  ScalarInt *pq = (ScalarInt *)a.qpos;
+  ScalarInt *pk = (ScalarInt *)a.kv_last;
+#pragma unroll
+  for (int c = 0; c < 64; c += 16) {
+    if (c + 16 <= a.rows) {
+      int o[16], q[16], k[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        o[j] = po[c + j];
+        q[j] = pq[c + j];
+        k[j] = pk[c + j];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (lane == c + j) {
+          m.org = o[j];
+          m.qp = q[j];
+          m.kl = k[j];
+        }
+      }
+    } else if (c < a.rows) {
+      // the last, partial chunk: rows past rows - 1 read row rows - 1 again
+      // (no branch per row, so the loads are waited for together)
+      int o[16], q[16], k[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int r = min(c + j, a.rows - 1);
+        o[j] = po[r];
+        q[j] = pq[r];
+        k[j] = pk[r];
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        if (lane == c + j && c + j < a.rows) {
+          m.org = o[j];
+          m.qp = q[j];
+          m.kl = k[j];
+        }
+      }
+    }
+  }
+  return m;
+}
+
+// The tile starting at row t0 from the lanes of rows_by_lane.
+__device__ __forceinline__ Tile tile_of_lanes(const DecodeArgs &a, const LaneRows &m, int t0, int lane) {
+  const int r = min(t0 + lane, 63);
+  const bool lrow = lane < a.rmax && t0 + lane < a.rows;
+  const int org_l = __shfl(m.org, r), qp_l = __shfl(m.qp, r), hi_l = __shfl(m.kl, r);
+  const int prev_origin = t0 > 0 ? __builtin_amdgcn_readlane(m.org, t0 - 1) : INT_MIN;
+  return tile_from(a, t0, lane, 0, lrow, org_l, qp_l, hi_l, prev_origin);
+}
+
+// The tile starting at row t0, its rows' metadata loaded (vector loads).
+__device__ __forceinline__ Tile tile_rows(const DecodeArgs &a, int t0, int lane, int force_rows = 0) {
+  const int span = force_rows > 0 ? force_rows : a.rmax;
+  const bool lrow = lane < span && t0 + lane < a.rows;
+  const int org_l = lrow ? a.page_origin[t0 + lane] : INT_MIN;
+  const int qp_l = lrow ? a.qpos[t0 + lane] : 0;
+  const int hi_l = lrow ? a.kv_last[t0 + lane] : -1;
+  const int prev_origin = force_rows == 0 && t0 > 0 ? a.page_origin[t0 - 1] : INT_MIN;
+  return tile_from(a, t0, lane, force_rows, lrow, org_l, qp_l, hi_l, prev_origin);
 }
 
 // Prefill: sub-tile p of the launch -> its first row and row count (0: none,
@@ -363,6 +442,24 @@ __device__ __forceinline__ int row_of_rank(const DecodeArgs &a, int p, int lane)
   return p;  // not reached
 }
 
+// row_of_rank from the lanes: the rank of lane r's row is the number of
+// rows that see more keys, plus the rows that see as many with a smaller
+// index -- the same order.
+__device__ __forceinline__ int rank_of_lanes(const DecodeArgs &a, const LaneRows &m, int p, int lane) {
+  int len = -1;
+  if (lane < a.rows) {
+    const int lo = a.window > 0 ? max(0, m.qp + 1 - a.window) : 0;
+    len = min(max(m.kl - lo + 1, 0), kRankLenMax);
+  }
+  int rank = 0;
+  for (int j = 0; j < a.rows; ++j) {
+    const int lj = __builtin_amdgcn_readlane(len, j);
+    rank += lj > len || (lj == len && j < lane) ? 1 : 0;
+  }
+  const uint64_t hit = __ballot(lane < a.rows && rank == p);
+  return hit ? static_cast<int>(__builtin_ctzll(hit)) : p;
+}
+
 // Split `split` of S covers pages [pbeg, pend) of the tile's visible page
 // range [lo_min / 16, hi_max / 16], cut into S contiguous near-equal chunks
 // from logical positions only (some may be empty).
@@ -376,28 +473,60 @@ __device__ __forceinline__ void split_range(const Tile &t, int split, int splits
   }
 }
 
+// Splits a tile uses of the call's S: one per kSplitPages pages of its
+// visible page range (at least 1, at most S).  Splits st .. S - 1 of the tile
+// do no work: they write no partial -- with the separate combine only an
+// empty (m, l) = (-inf, 0) in their slots, which the merge skips exactly --
+// and take no part in the fused merge, which reads st partials.  A tile of
+// one split writes its output directly when the merge is fused, and its slot
+// 0 for the combine otherwise (whose merge of one split gives the same bits:
+// weight exp2(0) = 1).
+constexpr int kSplitPages = 16;
+__host__ __device__ constexpr int splits_for_pages(int64_t pages, int64_t splits) {
+  const int64_t s = (pages + kSplitPages - 1) / kSplitPages;
+  return static_cast<int>(pages < 1 ? 1 : s < splits ? s : splits);
+}
+__device__ __forceinline__ int tile_splits(const Tile &t, int splits) {
+  if (t.hi_max < 0) return 1;
+  return splits_for_pages(t.hi_max / kPage - t.lo_min / kPage + 1, splits);
+}
+
+// The empty (m, l) of split `split` for the tile's columns (separate
+// combine; plain stores, read after the launch).
+__device__ __forceinline__ void mark_empty_split(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols,
+                                                 int cap, int split) {
+  for (int c = threadIdx.x; c < ncols; c += blockDim.x) {
+    const Column rc = tile_column(c, a.group, nrows, hb, cap);
+    const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
+    float *ml = a.part_ml + 2 * (th * a.splits + split);
+    ml[0] = -INFINITY;
+    ml[1] = 0.f;
+  }
+}
+
 // ---- fused merge: the last workgroup of a merge unit merges every split ----
-// Called by all threads once this workgroup's partial stores are issued.  The
-// unit's counter is a ticket: the workgroup that draws splits-1 merges and
-// resets the counter to zero.  Columns are taken CG at a time (CG * S <= NT):
+// Called by all threads once this workgroup's partial stores are issued; st
+// is the tile's split count.  The unit's counter is a ticket: the workgroup
+// that draws st - 1 merges the st partials and resets the counter to zero.  Columns are taken CG at a time (CG * S <= NT):
 // one round of loads fetches every (m, l) of the group, a second every partial
 // element; each thread keeps the eight group sums of its elements, which is
 // the combine kernel's arithmetic element for element.
 template <int HD, int NT>
-__device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap,
+__device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int st,
                             FusedScratch<NT> *fsp, int *s_is_last) {
   wait_all_memory();  // this workgroup's partial stores have completed
   __syncthreads();
   const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
   if (threadIdx.x == 0) {
     const int prev = __hip_atomic_fetch_add(&a.counters[unit], 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    *s_is_last = prev == a.splits - 1;
+    *s_is_last = prev == st - 1;
   }
   __syncthreads();
   if (!*s_is_last) return;
   FusedScratch<NT> &fs = *fsp;
   const LoadCoherent ld;
-  const int S = a.splits;
+  const int S = st;           // partials merged
+  const int SS = a.splits;    // slots per (row, head)
   const int tid = threadIdx.x;
   const int cg_max = max(1, min(ncols, NT / S));
   for (int c0 = 0; c0 < ncols; c0 += cg_max) {
@@ -407,8 +536,8 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
       const int c = idx / S, sp = idx - c * S;
       const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      const float m = ld(a.part_ml + (th * S + sp) * 2);
-      const float l = ld(a.part_ml + (th * S + sp) * 2 + 1);
+      const float m = ld(a.part_ml + (th * SS + sp) * 2);
+      const float l = ld(a.part_ml + (th * SS + sp) * 2 + 1);
       fs.l[idx] = l;
       fs.w[idx] = l > 0.f ? m : -INFINITY;
     }
@@ -448,7 +577,7 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
       const int c = idx / HD, d = idx - c * HD;
       const Column rc = tile_column(c0 + c, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      const float *o = a.part_o + th * S * HD + d;
+      const float *o = a.part_o + th * SS * HD + d;
       const float *w = fs.w + c * S;
       float num[kMergeGroups];
 #pragma unroll
@@ -485,7 +614,7 @@ constexpr float kRescaleSlack = 8.f;
 // The parallel fused merge (defined with the combine kernel below).
 template <int HD, int NT>
 __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
-                            int *s_word);
+                            int st, int *s_word);
 
 template <int HD>
 __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
@@ -511,45 +640,51 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   const int hb = b % a.hblocks;
   b /= a.hblocks;
   const int kh = b % a.nkv;
+  // ---- the tile: row metadata through the scalar cache in large ranked
+  // launches of up to 64 rows, else vector loads; Q is requested afterwards,
+  // with the first page-table window, so the two share one memory round
+  // trip ----
   int sub_rows = 0;
-  const int t0 = a.tile_row0 ? prefill_subtile(a, b / a.nkv, sub_rows) : row_of_rank(a, b / a.nkv, lane);
+  const int pos = b / a.nkv;
+  const bool lane_rows = !a.tile_row0 && a.rank_rows && a.rows <= 64;
+  LaneRows lr{INT_MIN, 0, -1};
+  if (lane_rows) lr = rows_by_lane(a, lane);
+  const int t0 = a.tile_row0   ? prefill_subtile(a, pos, sub_rows)
+                 : lane_rows ? rank_of_lanes(a, lr, pos, lane)
+                             : row_of_rank(a, pos, lane);
   if (a.tile_row0 && sub_rows == 0) return;
-
-  // ---- tile; Q for every possible column is requested in the same round ----
-  const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
-  bf16x8 qop[KJ];
-  {
-    const bool q_in = col0.on && t0 + col0.row < a.rows;
-    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (q_in ? col0.row : 0)) * a.nh + kh * a.group + col0.head) * HD;
-#pragma unroll
-    for (int j = 0; j < KJ; ++j) {
-      if (q_in) {
-        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
-      } else {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qop[j] = __builtin_bit_cast(bf16x8, z);
-      }
-    }
-  }
-  const Tile tile = tile_rows(a, t0, lane, sub_rows);
+  const Tile tile = lane_rows ? tile_of_lanes(a, lr, t0, lane) : tile_rows(a, t0, lane, sub_rows);
   if (!tile.lead) return;
   const int origin = tile.origin;
   const int nrows = tile.nrows;
   const int lo_l = tile.lo_l, hi_l = tile.hi_l;
+  const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
+  const int st = tile_splits(tile, a.splits);
+  if (split >= st) {
+    if (a.counters == nullptr) mark_empty_split(a, t0, kh, hb, nrows, ncols, 16, split);
+    return;
+  }
   int pbeg, pend;
-  split_range(tile, split, a.splits, pbeg, pend);
+  split_range(tile, split, st, pbeg, pend);
 
-  // ---- this lane's score column ----
+  // ---- this lane's score column and its Q (zero for a column without a row) ----
   const Column col = tile_column(ln, a.group, nrows, hb, 16);
   const int col_lo = __shfl(lo_l, col.row);
   // shuffle with every lane active, then drop columns without a row
   const int col_hi_any = __shfl(hi_l, col.row);
   const int col_hi = col.on ? col_hi_any : -1;
-  if (!col.on) {
+  bf16x8 qop[KJ];
+  {
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (col.on ? col.row : 0)) * a.nh + kh * a.group +
+                                  (col.on ? col.head : 0)) * HD;
 #pragma unroll
     for (int j = 0; j < KJ; ++j) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qop[j] = __builtin_bit_cast(bf16x8, z);
+      if (col.on) {
+        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[j] = __builtin_bit_cast(bf16x8, z);
+      }
     }
   }
 
@@ -758,8 +893,8 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   __syncthreads();
   if (wave == 0) take_state(0);
 
-  const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
-  const bool fused = a.splits > 1 && a.counters != nullptr;
+  const bool fused = st > 1 && a.counters != nullptr;
+  const bool direct = st == 1 && (a.splits == 1 || a.counters != nullptr);
   if (wave == 0) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -767,7 +902,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
       if (r >= ncols) continue;
       const Column rc = tile_column(r, a.group, nrows, hb, 16);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      if (a.splits == 1) {
+      if (direct) {
         const float l = lacc[i];
 #pragma unroll
         for (int jj = 0; jj < DJ; ++jj) {
@@ -793,12 +928,12 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   if constexpr (HD >= 256) {
     if (a.spin_ticks > 0) {
       __syncthreads();  // the V staging area is free for the merge scratch
-      owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, &s_is_last);
+      owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, st, &s_is_last);
       return;
     }
   }
-  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]),
-                            &s_is_last);
+  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, st,
+                            reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]), &s_is_last);
 }
 
 // ---------------------------------------------------------------------------
@@ -851,41 +986,44 @@ __global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
   const int hb = b % a.hblocks;
   b /= a.hblocks;
   const int kh = b % a.nkv;
-  const int t0 = row_of_rank(a, b / a.nkv, lane);
-
-  // ---- Q of this wave's slice for every possible column (first round trip) ----
-  const Column col0 = tile_column(ln, a.group, a.rmax, hb, 16);
-  bf16x8 qop[KS];
-  {
-    const bool q_in = col0.on && t0 + col0.row < a.rows;
-    const uint16_t *qrow =
-        a.q + (static_cast<int64_t>(t0 + (q_in ? col0.row : 0)) * a.nh + kh * a.group + col0.head) * HD + h0;
-#pragma unroll
-    for (int j = 0; j < KS; ++j) {
-      if (q_in) {
-        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
-      } else {
-        u32x4 z = {0u, 0u, 0u, 0u};
-        qop[j] = __builtin_bit_cast(bf16x8, z);
-      }
-    }
-  }
-  const Tile tile = tile_rows(a, t0, lane);
+  // ---- the tile (row metadata through the scalar cache in large ranked
+  // launches of up to 64 rows); Q follows, requested with the first
+  // page-table window ----
+  const int pos = b / a.nkv;
+  const bool lane_rows = a.rank_rows && a.rows <= 64;
+  LaneRows lr{INT_MIN, 0, -1};
+  if (lane_rows) lr = rows_by_lane(a, lane);
+  const int t0 = lane_rows ? rank_of_lanes(a, lr, pos, lane) : row_of_rank(a, pos, lane);
+  const Tile tile = lane_rows ? tile_of_lanes(a, lr, t0, lane) : tile_rows(a, t0, lane);
   if (!tile.lead) return;
   const int origin = tile.origin;
   const int nrows = tile.nrows;
+  const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
+  const int st = tile_splits(tile, a.splits);
+  if (split >= st) {
+    if (a.counters == nullptr) mark_empty_split(a, t0, kh, hb, nrows, ncols, 16, split);
+    return;
+  }
   int pbeg, pend;
-  split_range(tile, split, a.splits, pbeg, pend);
+  split_range(tile, split, st, pbeg, pend);
 
   const Column col = tile_column(ln, a.group, nrows, hb, 16);
   const int col_lo = __shfl(tile.lo_l, col.row);
   const int col_hi_any = __shfl(tile.hi_l, col.row);
   const int col_hi = col.on ? col_hi_any : -1;
-  if (!col.on) {
+  // Q of this wave's slice (zero for a column without a row)
+  bf16x8 qop[KS];
+  {
+    const uint16_t *qrow = a.q + (static_cast<int64_t>(t0 + (col.on ? col.row : 0)) * a.nh + kh * a.group +
+                                  (col.on ? col.head : 0)) * HD + h0;
 #pragma unroll
     for (int j = 0; j < KS; ++j) {
-      u32x4 z = {0u, 0u, 0u, 0u};
-      qop[j] = __builtin_bit_cast(bf16x8, z);
+      if (col.on) {
+        qop[j] = *reinterpret_cast<const bf16x8 *>(qrow + (4 * j + lc) * 8);
+      } else {
+        u32x4 z = {0u, 0u, 0u, 0u};
+        qop[j] = __builtin_bit_cast(bf16x8, z);
+      }
     }
   }
 
@@ -1067,15 +1205,15 @@ __global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
   if (lc == 0) xfer[wave][ln] = m_run;
   wave_lds_sync();
   const f32x4 mo = *reinterpret_cast<const f32x4 *>(&xfer[wave][4 * lc]);
-  const int ncols = a.group <= 16 ? nrows * a.group : min(16, a.group - hb * 16);
-  const bool fused = a.splits > 1 && a.counters != nullptr;
+  const bool fused = st > 1 && a.counters != nullptr;
+  const bool direct = st == 1 && (a.splits == 1 || a.counters != nullptr);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int r = 4 * lc + i;
     if (r >= ncols) continue;
     const Column rc = tile_column(r, a.group, nrows, hb, 16);
     const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-    if (a.splits == 1) {
+    if (direct) {
       const float l = lacc[i];
 #pragma unroll
       for (int u = 0; u < DS; ++u) {
@@ -1096,11 +1234,11 @@ __global__ __launch_bounds__(kThreads) void pgqa_slice_kernel(DecodeArgs a) {
   if (!fused) return;
   __syncthreads();  // the V staging area is free for the merge scratch
   if (a.spin_ticks > 0) {
-    owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, &s_is_last);
+    owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, st, &s_is_last);
     return;
   }
-  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]),
-                            &s_is_last);
+  fused_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, st,
+                            reinterpret_cast<FusedScratch<kThreads> *>(&vtile[0][0]), &s_is_last);
 }
 
 // ---- merge of one block of 32 consecutive hd elements of one (row, query head) ----
@@ -1128,14 +1266,15 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer
 // every S, is no faster in either merge and costs the combine 55 VGPRs).
 constexpr int kMergeBatch = 16;
 template <int CPOL, int BATCH>
-__device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, bool live) {
+__device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, bool live,
+                                             int S) {
   if (!live) return;
   const int g = lane >> 3, q = lane & 7;
-  const int S = a.splits;
   const int ni = (S + kMergeGroups - 1) / kMergeGroups;  // splits per group (at most)
   const __amdgpu_buffer_rsrc_t ro =
-      __builtin_amdgcn_make_buffer_rsrc(a.part_o + th * S * hd, 0, S * hd * 4, kBufferWord3);
-  const __amdgpu_buffer_rsrc_t rml = __builtin_amdgcn_make_buffer_rsrc(a.part_ml + th * S * 2, 0, S * 8, kBufferWord3);
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + th * a.splits * hd, 0, S * hd * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rml =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_ml + th * a.splits * 2, 0, S * 8, kBufferWord3);
   // (m, l) of the group's splits: the group's i-th split (s = g + 8 i) is
   // loaded by lane 8 g + (i mod 8), as its (i / 8)-th pair (past split S - 1:
   // split S - 1 again, never used)
@@ -1218,10 +1357,12 @@ __global__ __launch_bounds__(64) void pgqa_combine_kernel(DecodeArgs a, int hd) 
   const int chunks = hd / 32;
   const int64_t th = blockIdx.x / chunks;
   const int d0 = static_cast<int>(blockIdx.x - th * chunks) * 32;
-  merge_wave32<kCpolPlain, kMergeBatch>(a, th, d0, hd, threadIdx.x, true);
+  merge_wave32<kCpolPlain, kMergeBatch>(a, th, d0, hd, threadIdx.x, true, a.splits);
 }
 
 // ---- parallel fused merge of one unit (owned blocks) ----
+// S below is the tile's split count (pgqa_tile_splits): only those
+// workgroups of the unit take part.
 // The unit's outputs are cut into blocks of 32 elements and the blocks into
 // chunks of one block per wave of a workgroup; chunk c belongs to the
 // workgroup of split c mod S, whose waves merge its blocks one each.  Only
@@ -1262,7 +1403,7 @@ std::atomic<int> g_merge_wait_ticks{0};
 // this workgroup merged (the same in every thread).
 template <int HD, int NT>
 __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int nblocks, int cap, int first,
-                            int step) {
+                            int step, int S) {
   constexpr int per_col = HD / 32;
   constexpr int waves = NT / 64;
   const int lane = threadIdx.x & 63;
@@ -1273,7 +1414,7 @@ __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nro
     if (b < nblocks) {
       const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true);
+      merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true, S);
     }
     merged += min(waves, nblocks - c * waves);
   }
@@ -1282,12 +1423,12 @@ __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nro
 
 template <int HD, int NT>
 __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
-                            int *s_word) {
+                            int st, int *s_word) {
   const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
   int32_t *arrive = a.counters + unit;
   int32_t *flag = a.counters + kFlagBase + unit;
   int32_t *done = a.counters + kDoneBase + unit;
-  const int S = a.splits;
+  const int S = st;  // the tile's splits: arrivals, owners and partials merged
   const int nblocks = ncols * (HD / 32);
   const int nchunks = (nblocks + NT / 64 - 1) / (NT / 64);
   const int tid = threadIdx.x;
@@ -1318,7 +1459,7 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
   int first = split, step = S;
   for (int pass = 0; pass < 2; ++pass) {
     int merged = 0;
-    if (*s_word > 0) merged = merge_blocks<HD, NT>(a, t0, kh, hb, nrows, nblocks, cap, first, step);
+    if (*s_word > 0) merged = merge_blocks<HD, NT>(a, t0, kh, hb, nrows, nblocks, cap, first, step, S);
     __syncthreads();  // every thread has read s_word
     if (pass == 1) break;
     if (tid == 0) {
@@ -1395,7 +1536,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   __shared__ __attribute__((aligned(16))) f32x4 xscore[(WIDE ? 4 : 2) * kWaves][64];
   __shared__ float xfer[2 * kWaves][16];
   __shared__ int s_is_last;
-  __shared__ int3 s_tiles[64];  // tiles whose parallel merge follows the page loop (row, rows, columns)
+  __shared__ int4 s_tiles[64];  // tiles whose parallel merge follows the page loop (row, rows, columns, splits)
   static_assert(sizeof(FusedScratch<kSharedThreads>) <= sizeof(slot0), "merge scratch must fit a ring slot");
   static_assert(256 * MCH * 16 <= sizeof(slot0), "team merge round must fit a ring slot");
   // Ring slot I as a direct reference to its own object (no pointer table):
@@ -1443,9 +1584,15 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   for (int t0 = rb0; t0 < rb1;) {
     const Tile tile = tile_rows(a, t0, lane, sub_rows);
     const int nrows = tile.nrows;
-    int pbeg, pend;
-    split_range(tile, split, a.splits, pbeg, pend);
     const int ncols = a.group <= TCAP ? nrows * a.group : min(TCAP, a.group - hb * TCAP);
+    const int st = tile_splits(tile, a.splits);
+    if (split >= st) {
+      if (a.counters == nullptr) mark_empty_split(a, t0, kh, hb, nrows, ncols, TCAP, split);
+      t0 += nrows;
+      continue;
+    }
+    int pbeg, pend;
+    split_range(tile, split, st, pbeg, pend);
     const bool active = 16 * cbt < ncols;  // this wave's column block exists (wave-uniform)
 
     const Column col = tile_column(16 * cbt + ln, a.group, nrows, hb, TCAP);
@@ -1727,7 +1874,8 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
 
     // ---- results: team 0 (WIDE: both teams), this wave's hd slice of its
     // column block ----
-    const bool fused = !WIDE && a.splits > 1 && a.counters != nullptr;
+    const bool fused = !WIDE && st > 1 && a.counters != nullptr;
+    const bool direct = st == 1 && (a.splits == 1 || a.counters != nullptr);
     if ((WIDE || team == 0) && active) {
   #pragma unroll
       for (int i = 0; i < 4; ++i) {
@@ -1735,7 +1883,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
         if (r >= ncols) continue;
         const Column rc = tile_column(r, a.group, nrows, hb, TCAP);
         const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-        if (a.splits == 1) {
+        if (direct) {
           const float l = lo[i];
   #pragma unroll
           for (int u = 0; u < DS; ++u) {
@@ -1759,10 +1907,10 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
       if (fused) {
         if (a.spin_ticks > 0) {
           // merged after the page loop (its registers are free then)
-          if (tid == 0) s_tiles[n_tiles] = int3{t0, nrows, ncols};
+          if (tid == 0) s_tiles[n_tiles] = int4{t0, nrows, ncols, st};
           ++n_tiles;
         } else {
-          fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP,
+          fused_merge<HD, kSharedThreads>(a, t0, kh, hb, nrows, ncols, CAP, st,
                                           reinterpret_cast<FusedScratch<kSharedThreads> *>(slot0), &s_is_last);
         }
       }
@@ -1772,9 +1920,8 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   }
   if constexpr (WIDE) return;
   for (int i = 0; i < n_tiles; ++i) {
-    const int3 tl = s_tiles[i];
-    const int ncols_i = tl.z;
-    owned_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, ncols_i, CAP, split, &s_is_last);
+    const int4 tl = s_tiles[i];
+    owned_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, tl.z, CAP, split, tl.w, &s_is_last);
     __syncthreads();
   }
 }
@@ -2051,6 +2198,11 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   if (s > kMaxSplits) s = kMaxSplits;
   if (s < 1) s = 1;
   return static_cast<int32_t>(s);
+}
+
+int32_t pgqa_tile_splits(int64_t pages, int64_t splits) {
+  if (splits < 1) return 1;
+  return splits_for_pages(pages, splits < kMaxSplits ? splits : kMaxSplits);
 }
 
 uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_t hd) {

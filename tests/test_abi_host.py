@@ -24,7 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
             "pgqa_counter_capacity", "pgqa_last_error", "pgqa_attn_prefill", "pgqa_make_tiles",
             "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep", "pgqa_set_merge_wait_ticks",
-            "pgqa_attn_decode_noalloc"} <= set(names)
+            "pgqa_attn_decode_noalloc", "pgqa_tile_splits"} <= set(names)
     h = ctypes.CDLL(pg.LIB_PATH)
     for n in names:
         assert getattr(h, n, None) is not None, n
@@ -39,6 +39,16 @@ def test_part_bytes_formula():
     assert pg.decode_part_bytes(1, 16, 256, 512) == 16 * 256 * 514 * 4
     assert pg.decode_part_bytes(0, 16, 4, 64) == 0
     assert pg.decode_part_bytes(1, 1, 0, 64) == 0
+
+
+def test_tile_splits_rule():
+    """Splits a tile works on: ceil(pages / 16), at least 1, at most S (S
+    clamped to 256)."""
+    for pages in (0, 1, 15, 16, 17, 32, 33, 240, 241, 256, 257, 4096, 1 << 20):
+        for s in (1, 2, 3, 8, 16, 128, 256, 1000):
+            want = max(1, min(min(s, 256), -(-pages // 16)))
+            assert pg.tile_splits(pages, s) == want, (pages, s)
+    assert pg.tile_splits(100, 0) == 1 and pg.tile_splits(-5, 8) == 1
 
 
 def test_choose_splits_range_and_determinism():

@@ -311,3 +311,30 @@ def test_fused_merge_when_waiters_give_up(counters, name, splits):
     finally:
         pg.set_merge_wait_ticks(prev)
     assert per_head(sep, reference(name))[1] < TOL
+
+
+@pytest.mark.parametrize("name,splits", [("C4", 16), ("C5W4096", 256), ("PA", 64), ("C3", 256)])
+def test_tile_split_counts(name, splits):
+    """Each tile works on pgqa_tile_splits(its pages, S) of the S splits: in
+    the separate form, (row, head) slots below that count hold a split with
+    visible keys (l > 0) and the others the empty (m, l) = (-inf, 0).  Each
+    sequence here is one tile (its rows fit one tile of the call's plan)."""
+    import paged_gqa_decode_attn_amd as pg
+    w, dw = workload(name), device(name)
+    part = torch.empty(pg.decode_part_bytes(w.rows, w.nh, splits, w.hd), dtype=torch.uint8, device="cuda")
+    say(f"[gpu] {name} splits={splits}: partial slots")
+    dw.run(splits, counters=None, part=part)
+    ml = part.view(torch.float32)[w.rows * w.nh * splits * w.hd:].view(w.rows, w.nh, splits, 2).cpu().numpy()
+    rr = workloads.row_ranges(w)
+    lo = np.array([r[0] for r in rr])
+    hi = np.array([r[1] for r in rr])
+    for org in np.unique(w.page_origin):
+        rows = np.flatnonzero(w.page_origin == org)
+        assert np.all(np.diff(rows) == 1) and len(rows) <= 8
+        pages = int(hi[rows].max()) // 16 - int(lo[rows].min()) // 16 + 1
+        st = pg.tile_splits(pages, splits)
+        assert 1 <= st <= splits
+        used = ml[rows][:, :, :st]
+        assert np.all(used[..., 1] > 0), (name, org, st)
+        empty = ml[rows][:, :, st:]
+        assert np.all(np.isneginf(empty[..., 0])) and np.all(empty[..., 1] == 0), (name, org, st)
