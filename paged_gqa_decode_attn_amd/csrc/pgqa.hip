@@ -612,7 +612,7 @@ __device__ void fused_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
 constexpr float kRescaleSlack = 8.f;
 
 // The parallel fused merge (defined with the combine kernel below).
-template <int HD, int NT>
+template <int HD, int NT, bool WIDE = true>
 __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
                             int st, int *s_word);
 
@@ -1265,9 +1265,12 @@ constexpr int kBufferWord3 = 0x00020000;  // raw 32-bit buffer
 // Splits per group per round trip: 16 (measured: 32, one round trip for
 // every S, is no faster in either merge and costs the combine 55 VGPRs).
 constexpr int kMergeBatch = 16;
-template <int CPOL, int BATCH>
+template <int CPOL, int BATCH, int WB = 1>
 __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, bool live,
                                              int S) {
+  // WB > 1: the block is WB * 32 elements, lane (g, q) taking elements
+  // d0 + 32 w + 4 q .. + 3 for w < WB (BATCH splits of a group, each WB loads,
+  // per round trip).  Every element's arithmetic is the same as with WB = 1.
   if (!live) return;
   const int g = lane >> 3, q = lane & 7;
   const int ni = (S + kMergeGroups - 1) / kMergeGroups;  // splits per group (at most)
@@ -1290,14 +1293,16 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
                                              rml, min(g + kMergeGroups * i, S - 1) * 8, 0, CPOL));
     }
   }
-  f32x4 v[BATCH];
+  f32x4 v[BATCH][WB];
   auto load_batch = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < BATCH; ++i)
       if (i0 + i < ni)
-        v[i] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(
-                                             ro, (min(g + kMergeGroups * (i0 + i), S - 1) * hd + d0 + 4 * q) * 4, 0,
-                                             CPOL));
+#pragma unroll
+        for (int w = 0; w < WB; ++w)
+          v[i][w] = __builtin_bit_cast(
+              f32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                         ro, (min(g + kMergeGroups * (i0 + i), S - 1) * hd + d0 + 32 * w + 4 * q) * 4, 0, CPOL));
   };
   load_batch(0);
 #pragma unroll
@@ -1308,7 +1313,9 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
   float dg = 0.f;
-  f32x4 num = {0.f, 0.f, 0.f, 0.f};
+  f32x4 num[WB];
+#pragma unroll
+  for (int w = 0; w < WB; ++w) num[w] = f32x4{0.f, 0.f, 0.f, 0.f};
   const int lead = lane & ~7;  // lane 8 g
   auto chain = [&](int i0) __attribute__((always_inline)) {
 #pragma unroll
@@ -1322,7 +1329,9 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
           if (ws != 0.f) {
             dg = __builtin_fmaf(ws, l_s, dg);
 #pragma unroll
-            for (int c = 0; c < 4; ++c) num[c] = __builtin_fmaf(ws, v[i][c], num[c]);
+            for (int w = 0; w < WB; ++w)
+#pragma unroll
+              for (int c = 0; c < 4; ++c) num[w][c] = __builtin_fmaf(ws, v[i][w][c], num[w][c]);
           }
         }
       }
@@ -1338,17 +1347,24 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
   }
   // sums over the 8 groups in group order
   float den = 0.f;
-  f32x4 n = {0.f, 0.f, 0.f, 0.f};
+  f32x4 n[WB];
+#pragma unroll
+  for (int w = 0; w < WB; ++w) n[w] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
   for (int gg = 0; gg < kMergeGroups; ++gg) {
     den += __shfl(dg, gg * 8);
 #pragma unroll
-    for (int c = 0; c < 4; ++c) n[c] += __shfl(num[c], gg * 8 + q);
+    for (int w = 0; w < WB; ++w)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) n[w][c] += __shfl(num[w][c], gg * 8 + q);
   }
   if (g == 0) {
-    uint16_t *op = a.out + th * hd + d0 + 4 * q;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) op[c] = f32_to_bf16_rne(den > 0.f ? n[c] / den : 0.f);
+    for (int w = 0; w < WB; ++w) {
+      uint16_t *op = a.out + th * hd + d0 + 32 * w + 4 * q;
+#pragma unroll
+      for (int c = 0; c < 4; ++c) op[c] = f32_to_bf16_rne(den > 0.f ? n[w][c] / den : 0.f);
+    }
   }
 }
 
@@ -1401,10 +1417,10 @@ std::atomic<int> g_merge_wait_ticks{0};
 // c * waves + waves - 1 below nblocks, one per wave; block b: column
 // b / (HD / 32), elements (b mod (HD / 32)) 32 ..).  Returns how many blocks
 // this workgroup merged (the same in every thread).
-template <int HD, int NT>
+template <int HD, int NT, int WB>
 __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int nblocks, int cap, int first,
                             int step, int S) {
-  constexpr int per_col = HD / 32;
+  constexpr int per_col = HD / (32 * WB);
   constexpr int waves = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1414,22 +1430,23 @@ __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nro
     if (b < nblocks) {
       const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
-      merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true, S);
+      if constexpr (WB == 1) merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true, S);
+      else merge_wave32<kCpolDevice, kMergeBatch / WB, WB>(a, th, (b % per_col) * 32 * WB, HD, lane, true, S);
     }
     merged += min(waves, nblocks - c * waves);
   }
   return merged;
 }
 
-template <int HD, int NT>
-__device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
-                            int st, int *s_word) {
+template <int HD, int NT, int WB>
+__device__ void owned_merge_wb(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
+                               int st, int *s_word) {
   const int unit = (t0 * a.nkv + kh) * a.hblocks + hb;
   int32_t *arrive = a.counters + unit;
   int32_t *flag = a.counters + kFlagBase + unit;
   int32_t *done = a.counters + kDoneBase + unit;
   const int S = st;  // the tile's splits: arrivals, owners and partials merged
-  const int nblocks = ncols * (HD / 32);
+  const int nblocks = ncols * (HD / (32 * WB));
   const int nchunks = (nblocks + NT / 64 - 1) / (NT / 64);
   const int tid = threadIdx.x;
   wait_all_memory();  // this workgroup's partial stores have completed
@@ -1459,7 +1476,7 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
   int first = split, step = S;
   for (int pass = 0; pass < 2; ++pass) {
     int merged = 0;
-    if (*s_word > 0) merged = merge_blocks<HD, NT>(a, t0, kh, hb, nrows, nblocks, cap, first, step, S);
+    if (*s_word > 0) merged = merge_blocks<HD, NT, WB>(a, t0, kh, hb, nrows, nblocks, cap, first, step, S);
     __syncthreads();  // every thread has read s_word
     if (pass == 1) break;
     if (tid == 0) {
@@ -1477,6 +1494,16 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
     __hip_atomic_store(flag, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     __hip_atomic_store(done, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   }
+}
+
+// Up to 32 splits, blocks of 128 elements (a merge of a few splits is one
+// short round trip, so fewer, wider blocks leave fewer rounds per owner);
+// 32 elements otherwise.  WIDE false: 32 elements always.
+template <int HD, int NT, bool WIDE>
+__device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
+                            int st, int *s_word) {
+  if (WIDE && st <= 4 * kMergeGroups) owned_merge_wb<HD, NT, 4>(a, t0, kh, hb, nrows, ncols, cap, split, st, s_word);
+  else owned_merge_wb<HD, NT, 1>(a, t0, kh, hb, nrows, ncols, cap, split, st, s_word);
 }
 
 // ---------------------------------------------------------------------------
@@ -1921,7 +1948,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   if constexpr (WIDE) return;
   for (int i = 0; i < n_tiles; ++i) {
     const int4 tl = s_tiles[i];
-    owned_merge<HD, kSharedThreads>(a, tl.x, kh, hb, tl.y, tl.z, CAP, split, tl.w, &s_is_last);
+    owned_merge<HD, kSharedThreads, false>(a, tl.x, kh, hb, tl.y, tl.z, CAP, split, tl.w, &s_is_last);
     __syncthreads();
   }
 }
