@@ -70,9 +70,10 @@ uint64_t pgqa_decode_part_bytes(int64_t rows, int64_t nh, int64_t splits, int64_
  * leave the split of a row to the implementation).  A tile is a run of rows
  * on one sequence that attn_decode processes together; `pages` is the number
  * of KV pages its rows can see (the pages from the first visible key of any
- * of its rows to the last).  Result: min(splits, ceil(pages / 16)), at least
+ * of its rows to the last).  Result: min(splits, ceil(pages / 4)), at least
  * 1, with splits clamped to PGQA_MAX_SPLITS -- so every split of a tile
- * covers at least 16 pages (or all of them).  Splits of the tile past that
+ * covers at least 4 pages (or all of them), the floor pgqa_choose_splits
+ * itself keeps.  Splits of the tile past that
  * count do no work, and the merge reads only the partials of the others; a
  * tile of one split is written without a merge.  Never fails.
  */

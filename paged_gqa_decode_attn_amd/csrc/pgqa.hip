@@ -474,14 +474,16 @@ __device__ __forceinline__ void split_range(const Tile &t, int split, int splits
 }
 
 // Splits a tile uses of the call's S: one per kSplitPages pages of its
-// visible page range (at least 1, at most S).  Splits st .. S - 1 of the tile
+// visible page range (at least 1, at most S).  4 pages is the split
+// heuristic's own floor (its latency regime), so the counts it chooses are
+// kept; a tile far shorter than the call's longest row gives up the rest.  Splits st .. S - 1 of the tile
 // do no work: they write no partial -- with the separate combine only an
 // empty (m, l) = (-inf, 0) in their slots, which the merge skips exactly --
 // and take no part in the fused merge, which reads st partials.  A tile of
 // one split writes its output directly when the merge is fused, and its slot
 // 0 for the combine otherwise (whose merge of one split gives the same bits:
 // weight exp2(0) = 1).
-constexpr int kSplitPages = 16;
+constexpr int kSplitPages = 4;
 __host__ __device__ constexpr int splits_for_pages(int64_t pages, int64_t splits) {
   const int64_t s = (pages + kSplitPages - 1) / kSplitPages;
   return static_cast<int>(pages < 1 ? 1 : s < splits ? s : splits);

@@ -42,13 +42,21 @@ def test_part_bytes_formula():
 
 
 def test_tile_splits_rule():
-    """Splits a tile works on: ceil(pages / 16), at least 1, at most S (S
-    clamped to 256)."""
-    for pages in (0, 1, 15, 16, 17, 32, 33, 240, 241, 256, 257, 4096, 1 << 20):
+    """Splits a tile works on: ceil(pages / 4), at least 1, at most S (S
+    clamped to 256); every count pgqa_choose_splits gives a one-sequence call
+    is kept (it never gives fewer than 4 pages per split)."""
+    for pages in (0, 1, 3, 4, 5, 16, 17, 32, 33, 240, 241, 1024, 1025, 4096, 1 << 20):
         for s in (1, 2, 3, 8, 16, 128, 256, 1000):
-            want = max(1, min(min(s, 256), -(-pages // 16)))
+            want = max(1, min(min(s, 256), -(-pages // 4)))
             assert pg.tile_splits(pages, s) == want, (pages, s)
     assert pg.tile_splits(100, 0) == 1 and pg.tile_splits(-5, 8) == 1
+
+
+def test_tile_splits_keep_the_heuristic_counts():
+    for span in (16, 64, 700, 1024, 4096, 16384, 32768, 131072):
+        for rows, nkv in ((1, 1), (1, 2), (4, 8), (8, 1), (5, 8)):
+            s = pg.choose_splits(span, rows, nkv, rows)
+            assert pg.tile_splits(-(-span // 16), s) == s, (span, rows, nkv, s)
 
 
 def test_choose_splits_range_and_determinism():
