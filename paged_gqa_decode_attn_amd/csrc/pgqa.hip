@@ -1370,6 +1370,62 @@ __device__ __forceinline__ void merge_wave32(const DecodeArgs &a, int64_t th, in
   }
 }
 
+// The same arithmetic for up to 16 splits with one lane per 4 elements: lane l
+// takes elements d0 + 4 l .. + 3 (a block of 256) and loads every split's
+// partial and (m, l) itself (one round trip), then runs the 8 group chains
+// and their in-order sum on its own -- no exchange between lanes.
+constexpr int kLaneMergeSplits = 16;
+template <int CPOL>
+__device__ __forceinline__ void merge_lanes256(const DecodeArgs &a, int64_t th, int d0, int hd, int lane, int S) {
+  const __amdgpu_buffer_rsrc_t ro =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_o + th * a.splits * hd, 0, S * hd * 4, kBufferWord3);
+  const __amdgpu_buffer_rsrc_t rml =
+      __builtin_amdgcn_make_buffer_rsrc(a.part_ml + th * a.splits * 2, 0, S * 8, kBufferWord3);
+  f32x2 ml[kLaneMergeSplits];
+  f32x4 v[kLaneMergeSplits];
+#pragma unroll
+  for (int s = 0; s < kLaneMergeSplits; ++s) {
+    if (s < S) {
+      ml[s] = __builtin_bit_cast(f32x2, __builtin_amdgcn_raw_buffer_load_b64(rml, s * 8, 0, CPOL));
+      v[s] = __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(ro, (s * hd + d0 + 4 * lane) * 4, 0, CPOL));
+    }
+  }
+  float mx = -INFINITY;
+#pragma unroll
+  for (int s = 0; s < kLaneMergeSplits; ++s)
+    if (s < S && ml[s].y > 0.f) mx = fmaxf(mx, ml[s].x);
+  float dg[kMergeGroups];
+  f32x4 num[kMergeGroups];
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) {
+    dg[g] = 0.f;
+    num[g] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+#pragma unroll
+  for (int s = 0; s < kLaneMergeSplits; ++s) {
+    if (s < S) {
+      const int g = s % kMergeGroups;
+      const float ws = ml[s].y > 0.f ? fast_exp2(ml[s].x - mx) : 0.f;
+      if (ws != 0.f) {
+        dg[g] = __builtin_fmaf(ws, ml[s].y, dg[g]);
+#pragma unroll
+        for (int c = 0; c < 4; ++c) num[g][c] = __builtin_fmaf(ws, v[s][c], num[g][c]);
+      }
+    }
+  }
+  float den = 0.f;
+  f32x4 n = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int g = 0; g < kMergeGroups; ++g) {
+    den += dg[g];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) n[c] += num[g][c];
+  }
+  uint16_t *op = a.out + th * hd + d0 + 4 * lane;
+#pragma unroll
+  for (int c = 0; c < 4; ++c) op[c] = f32_to_bf16_rne(den > 0.f ? n[c] / den : 0.f);
+}
+
 // Separate merge: one wave per (row, query head, 32 hd elements).
 __global__ __launch_bounds__(64) void pgqa_combine_kernel(DecodeArgs a, int hd) {
   const int chunks = hd / 32;
@@ -1406,7 +1462,7 @@ __global__ __launch_bounds__(64) void pgqa_combine_kernel(DecodeArgs a, int hd) 
 // No workgroup waits on another for more than spin_ticks, and none needs
 // another to be resident: a launch larger than the device holds only merges
 // later.
-constexpr int64_t kParallelMergeBytes = int64_t(256) << 10;  // per-unit partials from which the merge goes parallel
+constexpr int64_t kParallelMergeBytes = int64_t(64) << 10;  // per-unit partials from which the merge goes parallel
 constexpr int kClaimSpinTicks = 2000;                        // 20 us
 constexpr int kFlagBase = 2048;  // ready flags: counters[kFlagBase + unit]
 constexpr int kDoneBase = 3072;  // done counts: counters[kDoneBase + unit]
@@ -1433,6 +1489,7 @@ __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nro
       const Column rc = tile_column(b / per_col, a.group, nrows, hb, cap);
       const int64_t th = static_cast<int64_t>(t0 + rc.row) * a.nh + kh * a.group + rc.head;
       if constexpr (WB == 1) merge_wave32<kCpolDevice, kMergeBatch>(a, th, (b % per_col) * 32, HD, lane, true, S);
+      else if constexpr (WB == 8) merge_lanes256<kCpolDevice>(a, th, (b % per_col) * 256, HD, lane, S);
       else merge_wave32<kCpolDevice, kMergeBatch / WB, WB>(a, th, (b % per_col) * 32 * WB, HD, lane, true, S);
     }
     merged += min(waves, nblocks - c * waves);
@@ -1498,12 +1555,19 @@ __device__ void owned_merge_wb(const DecodeArgs &a, int t0, int kh, int hb, int 
   }
 }
 
-// Up to 32 splits, blocks of 128 elements (a merge of a few splits is one
+// Up to 16 splits (hd 256 and 512), blocks of 256 elements merged lane by
+// lane; up to 32, blocks of 128 elements (a merge of a few splits is one
 // short round trip, so fewer, wider blocks leave fewer rounds per owner);
 // 32 elements otherwise.  WIDE false: 32 elements always.
 template <int HD, int NT, bool WIDE>
 __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
                             int st, int *s_word) {
+  if constexpr (WIDE && HD >= 256) {
+    if (st <= kLaneMergeSplits) {
+      owned_merge_wb<HD, NT, 8>(a, t0, kh, hb, nrows, ncols, cap, split, st, s_word);
+      return;
+    }
+  }
   if (WIDE && st <= 4 * kMergeGroups) owned_merge_wb<HD, NT, 4>(a, t0, kh, hb, nrows, ncols, cap, split, st, s_word);
   else owned_merge_wb<HD, NT, 1>(a, t0, kh, hb, nrows, ncols, cap, split, st, s_word);
 }
