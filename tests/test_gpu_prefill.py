@@ -32,8 +32,11 @@ def prefill_workload(name, ctx, nh, nkv, hd, window):
 
 
 CASES = [
-    # the page's two prefill runs (its PA and PB shapes)
+    # the page's two prefill runs (its PA and PB shapes); at hd 256 a launch
+    # of fewer than 512 (tile, kv head) units takes 64-column tiles
     ("pf_pa", 1500, 16, 8, 256, 1024),
+    # hd 256 with 512 units: the wide 128-column form
+    ("pf_wide256", 2048, 32, 16, 256, 128),
     ("pf_pb", 700, 16, 2, 512, 0),
     # the per-wave kernel (hd 64) and the shared-page kernel at hd 128, group 8
     ("pf_hd64", 300, 8, 2, 64, 50),
