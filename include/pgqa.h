@@ -118,10 +118,13 @@ int32_t pgqa_counter_capacity(void);
  *               int32 [pgqa_counter_capacity()], all zero before the first
  *               call, and the merge happens inside the decode launch: the last
  *               workgroup of each merge unit merges and resets its counter;
- *               when one unit's merge would read 2 MB or more of partials, the
- *               unit's workgroups wait briefly (at most 20 us each) for the
- *               last one and merge it together, claiming slices through the
- *               same counter.  Either way the buffer is all zero again when
+ *               when one unit's merge would read 64 KB or more of partials
+ *               (hd 256 and up in the per-wave kernel), the unit's
+ *               workgroups wait briefly (at most 20 us each, see
+ *               pgqa_set_merge_wait_ticks) for the last one and merge it
+ *               together, each its own blocks, through three counter words
+ *               per unit (entries unit, 2048 + unit and 3072 + unit, so
+ *               at most 1024 such units).  Either way the buffer is all zero again when
  *               the call completes and can be reused without clearing.  The
  *               result is the same as with NULL counters, bit for bit.  For
  *               calls with one or two merge units and many splits the

@@ -246,18 +246,17 @@ def test_edge_cases(counters, w):
 
 
 def merge_layout_workloads():
-    """Fused calls whose merge runs in parallel (2 MB or more of partials per
+    """Fused calls whose merge runs in parallel (64 KB or more of partials per
     merge unit) in other shapes than C3's and C5's: 300 units of 4 rows (hd
-    512, group 8) in a launch larger than the device holds at once, so units
-    complete one after another while their waiting workgroups hold CUs; and
-    units of one column (MHA, hd 512; 16-column tiles, so parallel from 64
-    splits) with only 8 slices for 64 or more workgroups; and 4 units of 8
-    columns (2 rows x group 4, hd 512) in the per-wave kernel, merged by the
-    last workgroup at 32 splits and by all of them from 64; and a batch of 8
-    sequences at hd 512, group 2, in the per-wave kernel (16 units, 1024 or
-    more workgroups: rows taken longest first, several rounds of workgroups
-    while earlier units wait for their merges).  Split counts that are not powers
-    of two are included."""
+    512, group 8; shared-page kernel) in a launch larger than the device
+    holds at once, so units complete one after another while their waiting
+    workgroups hold CUs; units of one column (MHA, hd 512) with fewer blocks
+    than workgroups; 4 units of 8 columns (2 rows x group 4, hd 512) in the
+    hd-sliced kernel; and a batch of 8 sequences at hd 512, group 2, in the
+    hd-sliced kernel (16 units, rows ranked from the scalar-cache metadata,
+    several rounds of workgroups while earlier units wait for their merges).
+    Split counts that are not powers of two are included; each tile uses
+    pgqa_tile_splits of them."""
     rng_seq = workloads.single_sequence
     return [(rng_seq("units300", ctx=1200, rows=300, nh=8, nkv=1, hd=512, window=0), (32, 37, 64)),
             (rng_seq("col1", ctx=2000, rows=1, nh=2, nkv=2, hd=512, window=0), (64, 100, 125)),
