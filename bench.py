@@ -169,12 +169,14 @@ def _probe_lib():
 
 
 def read_probe(sizes=(("contiguous_2GiB", 2 << 30, 0), ("contiguous_128MiB", 128 << 20, 0),
-                      ("scattered_4KB_2GiB", 2 << 30, 1)), steps=5, warmup=2):
+                      ("scattered_4KB_2GiB", 2 << 30, 1)), steps=5, warmup=2, points=None,
+               grid=(256, 512, 1024, 2048, 4096), in_flight=(4, 8, 16)):
     """The streaming-read ceiling of this GPU with the decode kernels' load form
     (16-byte nontemporal loads into registers; csrc/read_probe.hip): for each
     pattern, a sweep of grid sizes and loads in flight, each timed with HIP
     events over single launches after a 1 GiB eviction read; the best mean per
-    pattern is reported."""
+    pattern is reported.  ``points``, if a list, receives every point of the
+    sweep."""
     import torch
 
     h = _probe_lib()
@@ -186,9 +188,9 @@ def read_probe(sizes=(("contiguous_2GiB", 2 << 30, 0), ("contiguous_128MiB", 128
     res = {}
     for name, nbytes, scatter in sizes:
         best = None
-        for blocks in (256, 512, 1024, 2048, 4096):
-            for unroll in (4, 8, 16):
-                if scatter and unroll == 16:
+        for blocks in grid:
+            for unroll in in_flight:
+                if scatter and unroll == 16 and points is None:
                     continue
                 sink = torch.empty(blocks, dtype=torch.int32, device="cuda")
                 run = lambda: h.pgqa_probe_read(big.data_ptr(), nbytes, blocks, unroll, scatter, sink.data_ptr(),
@@ -206,6 +208,9 @@ def read_probe(sizes=(("contiguous_2GiB", 2 << 30, 0), ("contiguous_128MiB", 128
                 torch.cuda.synchronize()
                 ms = float(np.mean([a.elapsed_time(b) for a, b in ev]))
                 gbs = nbytes / (ms * 1e-3) / 1e9
+                if points is not None:
+                    points.append({"pattern": name, "workgroups": blocks, "loads_in_flight_per_lane": unroll,
+                                   "us": round(ms * 1e3, 2), "GB/s": round(gbs, 1)})
                 if best is None or gbs > best["GB/s"]:
                     best = {"GB/s": round(gbs, 1), "us": round(ms * 1e3, 2), "workgroups": blocks,
                             "loads_in_flight_per_lane": unroll, "bytes": nbytes}
@@ -352,6 +357,8 @@ def main():
                     help="only run a 1 GiB device-to-device copy 5 times (calibrates HBM byte counters)")
     ap.add_argument("--read-probe", action="store_true",
                     help="only run the streaming-read probe (csrc/read_probe.hip); one JSON line")
+    ap.add_argument("--probe-table", action="store_true",
+                    help="with --read-probe: print every point of a grid x loads-in-flight sweep")
     ap.add_argument("--probe-pattern", default="",
                     help="with --read-probe: one pattern only, as NAME:BYTES:SCATTER:WORKGROUPS:UNROLL "
                          "(for counter runs), e.g. c:1073741824:0:1024:8")
@@ -386,6 +393,16 @@ def main():
                 assert rc == 0, rc
             torch.cuda.synchronize()
             print(json.dumps({"read_probe": name, "bytes_per_launch": int(nbytes), "launches": args.steps}), flush=True)
+            return
+        if args.probe_table:
+            # every point of a wider sweep, one JSON line each, then the best per pattern
+            pts = []
+            best = read_probe(sizes=(("scattered_4KB_2GiB", 2 << 30, 1), ("contiguous_2GiB", 2 << 30, 0)),
+                              steps=4, points=pts, grid=(256, 512, 1024, 2048, 4096, 8192),
+                              in_flight=(1, 2, 4, 8, 16))
+            for p in pts:
+                print(json.dumps({"read_probe_point": p}), flush=True)
+            print(json.dumps({"read_probe": best}), flush=True)
             return
         print(json.dumps({"read_probe": read_probe()}), flush=True)
         return
