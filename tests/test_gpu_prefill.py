@@ -100,3 +100,25 @@ def test_prefill_skips_tiles_outside_the_rows():
     ref = oracle.decode(w)
     assert per_head(got[:90], ref[:90])[1] < TOL
     assert np.all(got[90:] == 0x1234)
+
+
+def test_prefill_full_8k_context_sampled_rows():
+    """The 8192-row causal context (nh 16, nkv 8, hd 256) that the benchmark
+    times, in the same launch (tiles from make_tiles): 72 rows -- both edges of
+    several 64-row tiles, the first and last rows, and rows drawn at random --
+    against the oracle computed for those rows alone; the permuted pool behind
+    a page map gives the same bits."""
+    w = prefill_workload("pf8k", 8192, 16, 8, 256, 0)
+    say(f"[gpu] prefill 8K: rows={w.rows} nh={w.nh} nkv={w.nkv} hd={w.hd}")
+    dw = DeviceWorkload(w)
+    got = dw.host(dw.prefill())
+    rng = np.random.default_rng(8192)
+    edges = [0, 1, 62, 63, 64, 65, 4095, 4096, 8126, 8127, 8128, 8129, 8190, 8191]
+    rows = sorted(set(edges) | set(int(r) for r in rng.choice(8192, 58, replace=False)))
+    ref = oracle.decode(oracle.rows_subset(w, rows))
+    whole, worst, at = per_head(got[rows], ref)
+    say(f"[gpu] prefill 8K: {len(rows)} sampled rows, rel_rms={whole:.3e} worst {at}: {worst:.3e}")
+    assert worst < TOL, (rows[at[0]], at[1], worst)
+    wm = workloads.with_page_map(w, first_live=0)
+    dm = DeviceWorkload(wm)
+    assert np.array_equal(dm.host(dm.prefill()), got), "8K prefill: page-map pool differs"
