@@ -169,7 +169,8 @@ def _probe_lib():
 
 
 def read_probe(sizes=(("contiguous_2GiB", 2 << 30, 0), ("contiguous_128MiB", 128 << 20, 0),
-                      ("scattered_4KB_2GiB", 2 << 30, 1)), steps=5, warmup=2, points=None,
+                      ("scattered_4KB_2GiB", 2 << 30, 1), ("paired_4KB_2GiB", 2 << 30, 2)), steps=5, warmup=2,
+               points=None,
                grid=(256, 512, 1024, 2048, 4096), in_flight=(4, 8, 16)):
     """The streaming-read ceiling of this GPU with the decode kernels' load form
     (16-byte nontemporal loads into registers; csrc/read_probe.hip): for each
@@ -397,7 +398,8 @@ def main():
         if args.probe_table:
             # every point of a wider sweep, one JSON line each, then the best per pattern
             pts = []
-            best = read_probe(sizes=(("scattered_4KB_2GiB", 2 << 30, 1), ("contiguous_2GiB", 2 << 30, 0)),
+            best = read_probe(sizes=(("scattered_4KB_2GiB", 2 << 30, 1), ("paired_4KB_2GiB", 2 << 30, 2),
+                                     ("contiguous_2GiB", 2 << 30, 0)),
                               steps=4, points=pts, grid=(256, 512, 1024, 2048, 4096, 8192),
                               in_flight=(1, 2, 4, 8, 16))
             for p in pts:
@@ -500,7 +502,9 @@ def main():
         # against what a plain streaming read reaches on this machine with the
         # kernels' own load form (labelled apart from the roofline, whose peak
         # is the 8 TB/s specification)
-        ref_pat = "scattered_4KB_2GiB" if args.config.upper().startswith("C4") else "contiguous_128MiB"
+        # the batched decode reads a randomly placed 4 KB K block and its V
+        # block from two pools: the paired pattern reads the same way
+        ref_pat = "paired_4KB_2GiB" if args.config.upper().startswith("C4") else "contiguous_128MiB"
         line["read_probe"] = {"what": "csrc/read_probe.hip: 16-byte nontemporal loads, every byte once, "
                                       "best of a grid/in-flight sweep", **probe,
                               "frac_of_probe": round(res["eff_gbs"] / probe[ref_pat]["GB/s"], 4),

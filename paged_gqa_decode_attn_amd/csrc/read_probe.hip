@@ -7,7 +7,11 @@
 //     permuted order (block j -> (j * 2654435761 + 12345) mod nblocks, a
 //     bijection for a power-of-two count), the way a batched decode reads
 //     randomly placed K/V pages; each workgroup takes a run of consecutive
-//     slots of that order.
+//     slots of that order;
+//   * paired 4 KB blocks: the two halves of the buffer stand for a K pool and
+//     a V pool; consecutive 4 KB slots read block j of the first half, then
+//     block j of the second half, j in the permuted order above -- a page's K
+//     then its V, as the per-wave decode kernel requests them.
 // Every byte is read exactly once per launch.  The loaded words are folded
 // with XOR and each workgroup writes one word to `sink`, so no load can be
 // dropped.  Not part of the attention path: a measuring instrument only,
@@ -20,7 +24,7 @@ namespace {
 
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
-template <int UNROLL, bool SCATTER>
+template <int UNROLL, int SCATTER>
 __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *buf, uint64_t n16, uint64_t per_block,
                                                          uint32_t nblocks4k, unsigned *sink) {
   const uint64_t b = blockIdx.x;
@@ -37,11 +41,17 @@ __global__ __launch_bounds__(256) void read_probe_kernel(const u32x4 *buf, uint6
     for (int u = 0; u < UNROLL; ++u) {
       uint64_t i = base + static_cast<uint64_t>(u) * 256 + threadIdx.x;
       if (i >= end) i = begin;  // past the end: read the first word again (cached)
-      if constexpr (SCATTER) {
+      if constexpr (SCATTER == 1) {
         // 16-byte word i of the slot order -> the word of the permuted 4 KB block
         const uint64_t slot = i >> 8, word = i & 255;
         const uint64_t blk = (slot * 2654435761ull + 12345ull) & (nblocks4k - 1);
         i = (blk << 8) | word;
+      } else if constexpr (SCATTER == 2) {
+        // slot 2 j + h -> block perm(j) of half h (nblocks4k / 2 blocks each)
+        const uint64_t slot = i >> 8, word = i & 255;
+        const uint64_t half = nblocks4k >> 1;
+        const uint64_t blk = ((slot >> 1) * 2654435761ull + 12345ull) & (half - 1);
+        i = (((slot & 1) * half + blk) << 8) | word;
       }
       v[u] = __builtin_nontemporal_load(buf + i);
     }
@@ -63,11 +73,14 @@ hipError_t launch(const void *buf, uint64_t bytes, int64_t blocks, int scatter, 
   const uint64_t per_block = (n16 + blocks - 1) / blocks;
   const uint32_t nblocks4k = static_cast<uint32_t>(bytes / 4096);
   const dim3 grid(static_cast<unsigned>(blocks)), blk(256);
-  if (scatter)
-    hipLaunchKernelGGL((read_probe_kernel<UNROLL, true>), grid, blk, 0, st, static_cast<const u32x4 *>(buf), n16,
+  if (scatter == 2)
+    hipLaunchKernelGGL((read_probe_kernel<UNROLL, 2>), grid, blk, 0, st, static_cast<const u32x4 *>(buf), n16,
+                       per_block, nblocks4k, sink);
+  else if (scatter)
+    hipLaunchKernelGGL((read_probe_kernel<UNROLL, 1>), grid, blk, 0, st, static_cast<const u32x4 *>(buf), n16,
                        per_block, nblocks4k, sink);
   else
-    hipLaunchKernelGGL((read_probe_kernel<UNROLL, false>), grid, blk, 0, st, static_cast<const u32x4 *>(buf), n16,
+    hipLaunchKernelGGL((read_probe_kernel<UNROLL, 0>), grid, blk, 0, st, static_cast<const u32x4 *>(buf), n16,
                        per_block, nblocks4k, sink);
   return hipGetLastError();
 }
@@ -89,9 +102,10 @@ int pgqa_probe_read(const void *buf, uint64_t bytes, int64_t blocks, int32_t unr
                     unsigned *sink, void *stream) {
   if (!buf || !sink || bytes == 0 || bytes % 4096 != 0 || blocks < 1 || blocks > (1 << 20)) return -1;
   if (reinterpret_cast<uintptr_t>(buf) & 15u) return -1;
+  if (scatter < 0 || scatter > 2) return -1;
   if (scatter) {
     const uint64_t nb = bytes / 4096;
-    if ((nb & (nb - 1)) != 0 || nb % static_cast<uint64_t>(blocks) != 0) return -1;
+    if (nb < 2 || (nb & (nb - 1)) != 0 || nb % static_cast<uint64_t>(blocks) != 0) return -1;
   }
   hipStream_t st = static_cast<hipStream_t>(stream);
   hipError_t e;
