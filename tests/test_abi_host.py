@@ -286,3 +286,28 @@ def test_prep_accepts_without_launch():
     assert rcall(tokens=0) == pg.OK
     assert rcall(tokens=0, rd=0, cos=None, sin=None) == pg.OK
     assert pg.last_error() == ""
+
+
+def test_read_probe_refuses_bad_patterns():
+    """The benchmark's streaming-read probe checks its arguments before it
+    launches anything: a pattern outside 0..2, a buffer that is not whole 4 KB
+    blocks or not 16-byte aligned, and scattered or paired patterns whose
+    block count is not a power of two divisible by the grid are refused."""
+    path = os.path.join(ROOT, "paged_gqa_decode_attn_amd", "libpgqa_probe.so")
+    if not os.path.exists(path):
+        pytest.skip("probe library not built")
+    h = ctypes.CDLL(path)
+    f = h.pgqa_probe_read
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_int32, ctypes.c_int32,
+                  ctypes.c_void_p, ctypes.c_void_p]
+    buf, sink = 1 << 20, 1 << 21  # never dereferenced: every call below is refused first
+    assert f(buf, 1 << 20, 16, 8, 3, sink, None) == -1   # no such pattern
+    assert f(buf, 1 << 20, 16, 8, -1, sink, None) == -1
+    assert f(buf, 5000, 1, 8, 0, sink, None) == -1       # not whole 4 KB blocks
+    assert f(buf + 8, 1 << 20, 16, 8, 0, sink, None) == -1  # misaligned
+    assert f(buf, 4096 * 3, 1, 8, 1, sink, None) == -1   # 3 blocks: not a power of two
+    assert f(buf, 4096 * 3, 1, 8, 2, sink, None) == -1
+    assert f(buf, 4096, 1, 8, 2, sink, None) == -1       # paired needs two blocks at least
+    assert f(buf, 1 << 20, 3, 8, 2, sink, None) == -1    # 256 blocks not divisible by 3 workgroups
+    assert f(buf, 1 << 20, 16, 3, 0, sink, None) == -1   # unroll 3 not built
