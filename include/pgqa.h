@@ -286,6 +286,21 @@ int pgqa_qk_rope_prep(void *q_out, void *k_pool, void *v_pool, const void *q_in,
  */
 int32_t pgqa_set_merge_wait_ticks(int32_t ticks);
 
+/*
+ * Test hook for the two page steps of narrow tiles (no page defines it).
+ * Tiles of at most 4 columns (columns = rows of the tile x heads per kv
+ * head) at hd 64 and 128 can run their scores and P.V either on MFMA, in
+ * 16-column blocks of which the tile fills at most 4, or on the vector ALU
+ * with packed bf16 dot products.  mode 0 (the default) takes the vector-ALU
+ * step in launches of more than 512 workgroups and MFMA otherwise; 1 takes
+ * the vector-ALU step wherever it applies; 2 never.  The two steps round
+ * differently, so their outputs differ in the last bits; each matches the
+ * definition to the same bound.  Applies to the calls enqueued after it, from
+ * any thread.  Returns the previous mode, or PGQA_EINVAL for a mode outside
+ * 0..2.
+ */
+int32_t pgqa_set_narrow_path(int32_t mode);
+
 /* Message for the last non-zero return on this thread ("" if none). */
 const char *pgqa_last_error(void);
 

@@ -11,7 +11,8 @@ GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
 ``counter_capacity``, ``attn_decode``, ``prefill_rows_per_tile``,
 ``make_tiles``, ``attn_prefill``; ``qk_rope_prep``, the QK-norm + RoPE step
 that fills the pool before decode; ``attn_decode_noalloc``, decode for
-callers that cannot allocate; ``set_merge_wait_ticks``, a test hook.
+callers that cannot allocate; ``set_merge_wait_ticks`` and
+``set_narrow_path``, test hooks.
 """
 from __future__ import annotations
 
@@ -67,6 +68,8 @@ def lib() -> ctypes.CDLL:
         h.pgqa_attn_decode_noalloc.argtypes = [p, p, p, p, p, p, p, p, i64, i64, i64, i64, i64, i64, p, p]
         h.pgqa_set_merge_wait_ticks.restype = ctypes.c_int32
         h.pgqa_set_merge_wait_ticks.argtypes = [ctypes.c_int32]
+        h.pgqa_set_narrow_path.restype = ctypes.c_int32
+        h.pgqa_set_narrow_path.argtypes = [ctypes.c_int32]
         h.pgqa_qk_rope_prep.restype = ctypes.c_int
         h.pgqa_qk_rope_prep.argtypes = [p] * 14 + [i64, i64, i64, i64, i64, ctypes.c_float, p]
         _lib = h
@@ -88,6 +91,16 @@ def decode_part_bytes(rows: int, nh: int, splits: int, hd: int) -> int:
 
 def counter_capacity() -> int:
     return int(lib().pgqa_counter_capacity())
+
+
+def set_narrow_path(mode: int) -> int:
+    """Test hook (``pgqa_set_narrow_path``): page step of tiles of at most 4
+    columns at hd 64/128 -- 0 by launch size (default), 1 vector ALU, 2 MFMA;
+    returns the previous mode."""
+    rc = int(lib().pgqa_set_narrow_path(mode))
+    if rc < 0:
+        raise PgqaError(rc, "mode must be 0, 1 or 2")
+    return rc
 
 
 def set_merge_wait_ticks(ticks: int) -> int:

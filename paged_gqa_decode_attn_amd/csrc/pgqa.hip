@@ -181,6 +181,48 @@ __device__ __forceinline__ s16x4 pack_weights(float p0, float p1, float p2, floa
                static_cast<short>(u1 >> 16)};
 }
 
+// Two bf16 packed in a 32-bit word, as the operand of v_dot2_f32_bf16.  (A
+// bit cast applied directly to an element of a vector value compiled to a
+// read of element 0 with this toolchain; the copy goes through a scalar.)
+__device__ __forceinline__ bf16x2 as_bf16x2(unsigned u) {
+  bf16x2 r;
+  __builtin_memcpy(&r, &u, 4);
+  return r;
+}
+
+// DPP lane moves within 16-lane rows: row_ror:8 (lane i <- i ^ 8),
+// row_half_mirror (i <- 7 - i within 8), quad_perm [2,3,0,1] (i <- i ^ 2) and
+// [1,0,3,2] (i <- i ^ 1).
+constexpr int kDppRor8 = 0x128, kDppHalfMirror = 0x141, kDppXor2 = 0x4E, kDppXor1 = 0xB1;
+template <int CTRL>
+__device__ __forceinline__ float dpp_move(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xf, 0xf, false));
+}
+// One level of a transposing sum over lane pairs (i, partner(i)) whose
+// `upper` flags differ: of its N values the lane keeps the upper half if
+// `upper`, else the lower, and adds the partner's copy of that half.  After
+// log2(N) such levels over distinct lane bits each lane holds one full sum,
+// the one whose index has the lane's bits.
+template <int CTRL, int N>
+__device__ __forceinline__ void fold_half(float *v, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float lo = v[i], hi = v[i + N / 2];
+    const float keep = upper ? hi : lo, send = upper ? lo : hi;
+    v[i] = keep + dpp_move<CTRL>(send);
+  }
+}
+// The same level for partners across rows (lane ^ OFF, OFF 16 or 32).
+template <int OFF, int N>
+__device__ __forceinline__ void fold_half_xor(float *v, bool upper) {
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    const float lo = v[i], hi = v[i + N / 2];
+    const float keep = upper ? hi : lo, send = upper ? lo : hi;
+    v[i] = keep + __shfl_xor(send, OFF);
+  }
+}
+
 // Agent-coherent 32-bit accesses for the partial results.  The stores go past
 // this XCD's L2 (write-through), so the fused merge needs no L2 write-back
 // fence -- its ordering comes from waiting for the stores to complete before
@@ -618,7 +660,16 @@ template <int HD, int NT, bool WIDE = true>
 __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int ncols, int cap, int split,
                             int st, int *s_word);
 
-template <int HD>
+// Tiles of at most this many columns may take the vector-ALU page step.
+constexpr int kNarrowCols = 4;
+
+// VALU = false: scores and P.V on MFMA, 16-column tiles.
+// VALU = true (hd 64 and 128, tiles of at most kNarrowCols columns): the page
+// step runs on the vector ALU with packed bf16 dot products
+// (v_dot2_f32_bf16), cross-lane sums through DPP, and no LDS staging of V;
+// the wave's state is moved into the MFMA form's output layout at the end,
+// so the merges and the epilogue are shared.
+template <int HD, bool VALU = false>
 __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;   // QK^T MFMA steps (32 hd elements each)
   constexpr int DJ = HD / 16;   // PV MFMA output blocks (16 hd columns each)
@@ -690,6 +741,42 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
     }
   }
 
+  // ---- vector-ALU form: K and V both arrive as 16-byte chunks, lane l of
+  // load j holding chunk cl = l % CH of token TPL*j + tg (tg = l / CH).  A
+  // lane computes the partial dot products of its chunk for all NLD tokens
+  // and kNarrowCols columns; a transposing sum over the CH lanes of a token
+  // row leaves lane l with the full score of column vc = cl % 4 and token
+  // vtok.  The weights go through LDS (64 floats); each lane then accumulates
+  // P.V for its own chunk over its NLD tokens, and the tg lanes of a chunk
+  // are summed once, after the last page. ----
+  constexpr int CH = HD / 8;        // 16-byte chunks per token row
+  constexpr int TPL = 64 / CH;      // tokens per 64-lane load
+  constexpr int NLD = kPage / TPL;  // loads per page, of K and of V
+  static_assert(!VALU || ((HD == 64 || HD == 128) && NLD * kNarrowCols == CH && NLD == VLD),
+                "the vector-ALU form is built for hd 64 and 128");
+  const int cl = lane % CH, tg = lane / CH;
+  const int vc = cl % kNarrowCols;                 // score column of this lane
+  const int vtok = TPL * (cl / kNarrowCols) + tg;  // and its token in the page
+  const Column vcol = tile_column(vc, a.group, nrows, hb, 16);
+  const int vcol_lo = __shfl(lo_l, vcol.row);
+  const int vcol_hi_any = __shfl(hi_l, vcol.row);
+  const int vcol_hi = vcol.on ? vcol_hi_any : -1;
+  u32x4 qv[kNarrowCols];               // Q chunk cl of every column
+  float vacc[kNarrowCols][8];          // o[column][8 cl + e] over this lane's tokens
+  float vl = 0.f, vm = -INFINITY;      // weight sum of this lane's (token, column); reference max of column vc
+  if constexpr (VALU) {
+#pragma unroll
+    for (int c = 0; c < kNarrowCols; ++c) {
+      const Column cc = tile_column(c, a.group, nrows, hb, 16);
+      qv[c] = u32x4{0u, 0u, 0u, 0u};
+      if (cc.on)
+        qv[c] = *reinterpret_cast<const u32x4 *>(
+            a.q + (static_cast<int64_t>(t0 + cc.row) * a.nh + kh * a.group + cc.head) * HD + cl * 8);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) vacc[c][e] = 0.f;
+    }
+  }
+
   float m_run = -INFINITY;  // reference max (log2 units) of column ln
   f32x4 oacc[DJ];           // rows 4*lc+i of the column block, hd column 16*jj+ln
   f32x4 lacc = {0.f, 0.f, 0.f, 0.f};
@@ -732,12 +819,111 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
     const int64_t page_off = static_cast<int64_t>(phys) * page_elems + kv_head_off;
     const uint16_t *kp = a.k_pool + page_off;
     const uint16_t *vp = a.v_pool + page_off;
+    if constexpr (VALU) {
 #pragma unroll
-    for (int j = 0; j < KJ; ++j)
-      kop[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(kp + ln * HD + (4 * j + lc) * 8));
+      for (int j = 0; j < KJ; ++j)
+        kop[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(kp + (j * 64 + lane) * 8));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KJ; ++j)
+        kop[j] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8 *>(kp + ln * HD + (4 * j + lc) * 8));
+    }
 #pragma unroll
     for (int j = 0; j < VLD; ++j)
       vreg[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(vp + (j * 64 + lane) * 8));
+  };
+  // The vector-ALU page step (same masking, lazy rescale and bf16 weights as
+  // the MFMA step below).
+  auto compute_page_valu = [&](int k, const bf16x8(&kop)[KJ], const u32x4(&vreg)[VLD]) {
+    const int p = first + kWaves * k;
+    const bool full = p >= tile.fp0 && p < tile.fp1;
+    float part[NLD * kNarrowCols];  // index j * 4 + column
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) {
+      const u32x4 kw = __builtin_bit_cast(u32x4, kop[j]);
+#pragma unroll
+      for (int c = 0; c < kNarrowCols; ++c) {
+        float sdot = 0.f;
+#pragma unroll
+        for (int d = 0; d < 4; ++d)
+          sdot = __builtin_amdgcn_fdot2_f32_bf16(as_bf16x2(kw[d]), as_bf16x2(qv[c][d]), sdot, false);
+        part[j * kNarrowCols + c] = sdot;
+      }
+    }
+    // sum over the CH lanes of a token row: lane bit 3 (hd 128), 2, 1, 0
+    if constexpr (CH == 16) fold_half<kDppRor8, 16>(part, (lane & 8) != 0);
+    fold_half<kDppHalfMirror, 8>(part, (lane & 4) != 0);
+    fold_half<kDppXor2, 4>(part, (lane & 2) != 0);
+    fold_half<kDppXor1, 2>(part, (lane & 1) != 0);
+    bool vis = true;
+    uint64_t bal = ~0ull;
+    if (!full) {
+      const int pos = p * kPage + vtok;
+      vis = vcol.on && pos >= vcol_lo && pos <= vcol_hi;
+      bal = __ballot(vis);
+      if (bal == 0) return;
+    }
+    const float sv = vis ? part[0] : -INFINITY;
+    if (__ballot(sv * kLog2e > vm + kRescaleSlack) != 0) {
+      // the column's max over its 16 lanes (lane bits 2-5)
+      float mx = sv;
+      mx = fmaxf(mx, __shfl_xor(mx, 4));
+      mx = fmaxf(mx, __shfl_xor(mx, 8));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m2 = mx * kLog2e;
+      const bool grow = m2 > vm + kRescaleSlack;
+      const float m_new = grow ? m2 : vm;
+      const float alpha = grow ? fast_exp2(vm - m_new) : 1.f;
+      vm = m_new;
+      vl *= alpha;
+#pragma unroll
+      for (int c = 0; c < kNarrowCols; ++c) {
+        const float ac = __shfl(alpha, c);  // lane c holds column c
+#pragma unroll
+        for (int e = 0; e < 8; ++e) vacc[c][e] *= ac;
+      }
+    }
+    float pw = fast_exp2(__builtin_fmaf(sv, kLog2e, -vm));
+    if (!full) pw = sv == -INFINITY ? 0.f : pw;
+    {
+      // the sum takes the bf16-rounded weight, as P.V does
+      const bf16x2 pb = __builtin_convertvector(f32x2{pw, 0.f}, bf16x2);
+      vl += __uint_as_float(__builtin_bit_cast(unsigned, pb) << 16);
+    }
+    float *pbuf = reinterpret_cast<float *>(vt);
+    pbuf[lane] = pw;
+    wave_lds_sync();
+    // weights of this lane's tokens: (token TPL*j + tg, column c) sits in lane
+    // tg*CH + 4j + c
+    f32x4 pj[NLD];
+#pragma unroll
+    for (int j = 0; j < NLD; ++j) pj[j] = reinterpret_cast<const f32x4 *>(pbuf + tg * CH)[j];
+#pragma unroll
+    for (int j2 = 0; j2 < NLD / 2; ++j2) {
+      const int j0 = 2 * j2, j1 = 2 * j2 + 1;
+      u32x4 v0 = vreg[j0], v1 = vreg[j1];
+      if (!full) {
+        // tokens no column sees may hold NaN
+        if (((bal >> (tg * CH + kNarrowCols * j0)) & 0xfull) == 0) v0 = u32x4{0u, 0u, 0u, 0u};
+        if (((bal >> (tg * CH + kNarrowCols * j1)) & 0xfull) == 0) v1 = u32x4{0u, 0u, 0u, 0u};
+      }
+      // element e of both tokens in one word: (v0[e], v1[e])
+      unsigned vpair[8];
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        vpair[2 * d] = __builtin_amdgcn_perm(v1[d], v0[d], 0x05040100u);
+        vpair[2 * d + 1] = __builtin_amdgcn_perm(v1[d], v0[d], 0x07060302u);
+      }
+#pragma unroll
+      for (int c = 0; c < kNarrowCols; ++c) {
+        const bf16x2 pp = __builtin_convertvector(f32x2{pj[j0][c], pj[j1][c]}, bf16x2);
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+          vacc[c][e] = __builtin_amdgcn_fdot2_f32_bf16(pp, as_bf16x2(vpair[e]), vacc[c][e], false);
+      }
+    }
+    wave_lds_sync();
   };
   auto compute_page = [&](int k, const bf16x8(&kop)[KJ], const u32x4(&vreg)[VLD]) {
     const int p = first + kWaves * k;
@@ -834,9 +1020,17 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
       u32x4 vB[VLD];
       for (int k = 0; k < wn; k += 2) {
         load_page(min(k + 1, wn - 1), kB, vB);
-        compute_page(w0 + k, kA, vA);
+        if constexpr (VALU)
+          compute_page_valu(w0 + k, kA, vA);
+        else
+          compute_page(w0 + k, kA, vA);
         load_page(min(k + 2, wn - 1), kA, vA);
-        if (k + 1 < wn) compute_page(w0 + k + 1, kB, vB);
+        if (k + 1 < wn) {
+          if constexpr (VALU)
+            compute_page_valu(w0 + k + 1, kB, vB);
+          else
+            compute_page(w0 + k + 1, kB, vB);
+        }
       }
     } else {
       for (int k = 0; k < wn; ++k) {
@@ -847,6 +1041,45 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
     wait_all_memory();
   }
 
+  if constexpr (VALU) {
+    // P.V partials: transposing sum over the lanes of one chunk (lane bits
+    // 5, 4, and 3 at hd 64) leaves each lane NKEEP outputs of one column
+    float fv[kNarrowCols * 8];
+#pragma unroll
+    for (int c = 0; c < kNarrowCols; ++c)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) fv[c * 8 + e] = vacc[c][e];
+    fold_half_xor<32, 32>(fv, (lane & 32) != 0);
+    fold_half_xor<16, 16>(fv, (lane & 16) != 0);
+    if constexpr (CH == 8) fold_half<kDppRor8, 8>(fv, (lane & 8) != 0);
+    constexpr int NKEEP = CH == 8 ? 4 : 8;
+    const int fcol = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
+    const int fe0 = CH == 8 ? ((lane >> 3) & 1) * 4 : 0;
+    // weight sums over each column's 16 lanes
+    vl += __shfl_xor(vl, 4);
+    vl += __shfl_xor(vl, 8);
+    vl += __shfl_xor(vl, 16);
+    vl += __shfl_xor(vl, 32);
+    // into the MFMA output layout through the wave's LDS area:
+    // o[column][hd], then the columns' sums and reference maxes
+    float *ob = reinterpret_cast<float *>(vt);
+    static_assert((kNarrowCols * HD + 2 * kNarrowCols) * 4 <= kPage * VSTR * 2, "state must fit the V staging area");
+#pragma unroll
+    for (int i = 0; i < NKEEP; ++i) ob[fcol * HD + cl * 8 + fe0 + i] = fv[i];
+    if (lane < kNarrowCols) {
+      ob[kNarrowCols * HD + lane] = vl;
+      ob[kNarrowCols * HD + kNarrowCols + lane] = vm;
+    }
+    wave_lds_sync();
+#pragma unroll
+    for (int jj = 0; jj < DJ; ++jj)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) oacc[jj][i] = lc == 0 ? ob[i * HD + 16 * jj + ln] : 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lacc[i] = lc == 0 ? ob[kNarrowCols * HD + i] : 0.f;
+    m_run = ln < kNarrowCols ? ob[kNarrowCols * HD + kNarrowCols + ln] : -INFINITY;
+    wave_lds_sync();
+  }
   // ---- reference max into the output layout ----
   if (lc == 0) xfer[wave][ln] = m_run;
   wave_lds_sync();
@@ -1470,6 +1703,9 @@ constexpr int kOwnedMergeUnits = 1024;  // units the three-word layout holds
 // Bound of the parallel merge's waits for the calls that follow, set by
 // pgqa_set_merge_wait_ticks (0: kClaimSpinTicks).
 std::atomic<int> g_merge_wait_ticks{0};
+// Page step of narrow tiles (pgqa_set_narrow_path): 0 chooses by launch size,
+// 1 takes the vector-ALU step wherever it applies, 2 never.
+std::atomic<int> g_narrow_path{0};
 
 // Chunks first, first + step, ... of the unit (chunk c: blocks c * waves ..
 // c * waves + waves - 1 below nblocks, one per wave; block b: column
@@ -2038,6 +2274,7 @@ struct Plan {
   int cap;      // columns per tile
   int rmax;     // rows per tile
   int hblocks;  // head blocks per kv head
+  int valu = 0; // per-wave kernel with the vector-ALU page step
 };
 Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   Plan p;
@@ -2115,6 +2352,12 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
     if (p.kind != 2) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pgqa_slice_kernel<HD>, grid, block, 0, stream, a);
   } else {
+    if constexpr (HD <= 128) {
+      if (p.valu) {
+        hipLaunchKernelGGL((pgqa_wave_kernel<HD, true>), grid, block, 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
   }
   return hipGetLastError();
@@ -2188,7 +2431,7 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   if (reinterpret_cast<uintptr_t>(out) & 1u) return fail(PGQA_EINVAL, "out must be 2-byte aligned");
 
   const int64_t group = nh / nkv;
-  const Plan plan = make_plan(rows, group, hd, splits);
+  Plan plan = make_plan(rows, group, hd, splits);
   // the per-wave kernel's workgroups each take one row (working only if it
   // starts a tile); the shared-page kernel's an rmax-aligned block of rows
   const int64_t grid_rows = plan.kind == 1 ? (rows + plan.rmax - 1) / plan.rmax : rows;
@@ -2203,6 +2446,20 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   const int64_t block_threads = plan.kind == 1 ? kSharedThreads : kThreads;
   if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
+  // Tiles of at most 4 columns (one row of a group of up to 4 heads, or a few
+  // rows of a narrower group) at hd 64 and 128 take the vector-ALU page step
+  // in launches of more than kRankMinBlocks workgroups: measured level with
+  // the MFMA step at hd 128 and 4% faster at hd 64 on batched decode, but
+  // 1.6 us slower on a one-workgroup call, so smaller launches keep MFMA.
+  // Rows per tile then drop to 4 / group, so no tile has more columns.
+  {
+    const int mode = g_narrow_path.load(std::memory_order_relaxed);
+    const bool fits = plan.kind == 0 && (hd == 64 || hd == 128) && group <= kNarrowCols;
+    if (fits && mode != 2 && (mode == 1 || blocks > kRankMinBlocks)) {
+      plan.valu = 1;
+      plan.rmax = static_cast<int>(kNarrowCols / group);
+    }
+  }
   const int64_t combine_blocks = rows * nh * (hd / 32);
   if (splits > 1 && !counters && combine_blocks * 64 > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "combine grid of %lld workgroups too large", (long long)combine_blocks);
@@ -2315,6 +2572,11 @@ const char *pgqa_last_error(void) { return pgqa_detail::error_text(); }
 int32_t pgqa_set_merge_wait_ticks(int32_t ticks) {
   if (ticks < 0) return PGQA_EINVAL;
   return g_merge_wait_ticks.exchange(ticks, std::memory_order_relaxed);
+}
+
+int32_t pgqa_set_narrow_path(int32_t mode) {
+  if (mode < 0 || mode > 2) return PGQA_EINVAL;
+  return g_narrow_path.exchange(mode, std::memory_order_relaxed);
 }
 
 int pgqa_attn_decode(void *out, void *part, const void *q, const void *k_pool, const void *v_pool,

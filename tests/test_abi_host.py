@@ -24,6 +24,7 @@ def test_library_exports_every_declared_symbol():
     assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
             "pgqa_counter_capacity", "pgqa_last_error", "pgqa_attn_prefill", "pgqa_make_tiles",
             "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep", "pgqa_set_merge_wait_ticks",
+            "pgqa_set_narrow_path",
             "pgqa_attn_decode_noalloc", "pgqa_tile_splits"} <= set(names)
     h = ctypes.CDLL(pg.LIB_PATH)
     for n in names:
@@ -182,6 +183,19 @@ def test_merge_wait_ticks_hook():
             pg.set_merge_wait_ticks(-1)
     finally:
         pg.set_merge_wait_ticks(prev)
+
+
+def test_narrow_path_hook():
+    prev = pg.set_narrow_path(1)
+    try:
+        assert pg.set_narrow_path(2) == 1
+        assert pg.set_narrow_path(0) == 2
+        for bad in (-1, 3):
+            with pytest.raises(pg.PgqaError):
+                pg.set_narrow_path(bad)
+        assert pg.set_narrow_path(0) == 0
+    finally:
+        pg.set_narrow_path(prev)
 
 
 def test_missing_library_is_loud(tmp_path, monkeypatch):
