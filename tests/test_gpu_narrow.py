@@ -102,10 +102,16 @@ def test_narrow_random_shapes(counters, path, i):
         assert np.array_equal(dm.host(dm.run(splits, counters=None)), outs[step]), f"case {i}: page map differs"
 
 
-@pytest.mark.parametrize("name,splits", [("C1", 1), ("C1", 4), ("C4", 3), ("C4NAN", 3)])
+def narrow_workload(name):
+    if name == "B64HD64":  # a 64-sequence batch at hd 64 (the shape where the vector-ALU step is fastest)
+        return workloads.batched("B64HD64", nseq=64, lmin=512, lmax=4096, nh=32, nkv=8, hd=64)
+    return workloads.make(name)
+
+
+@pytest.mark.parametrize("name,splits", [("C1", 1), ("C1", 4), ("C4", 3), ("C4NAN", 3), ("B64HD64", 3)])
 def test_narrow_configurations(counters, path, name, splits):
     """Both steps on the named narrow configurations, and the default choice."""
-    w = workloads.make(name)
+    w = narrow_workload(name)
     ref = oracle.decode(w)
     dw = DeviceWorkload(w)
     outs = {}
