@@ -158,6 +158,8 @@ def run_config(name, steps, warmup, mode, splits_override, flush):
 def _probe_lib():
     import ctypes
 
+    import torch  # noqa: F401  (the probe binds to torch's HIP runtime, as libpgqa.so does)
+
     path = os.path.join(ROOT, "paged_gqa_decode_attn_amd", "libpgqa_probe.so")
     if not os.path.exists(path):
         raise RuntimeError(f"{path} is not built; run __graft_entry__.build()")

@@ -43,6 +43,14 @@ def lib() -> ctypes.CDLL:
         if not os.path.exists(LIB_PATH):
             raise PgqaError(EINVAL, f"{LIB_PATH} is not built; run __graft_entry__.build() "
                                     "or python -m paged_gqa_decode_attn_amd._build")
+        # One HIP runtime per process: torch ships its own copy of the runtime
+        # under the same soname, and the library must bind to that one.  Loaded
+        # first, the library would pull in the system copy and torch would then
+        # load its own beside it, with separate device state.
+        try:
+            import torch  # noqa: F401
+        except ImportError:
+            pass
         h = ctypes.CDLL(LIB_PATH)
         i64, p = ctypes.c_int64, ctypes.c_void_p
         h.pgqa_choose_splits.restype = ctypes.c_int32

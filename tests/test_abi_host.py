@@ -5,6 +5,8 @@ anything touches the HIP runtime, so they are safe without a device."""
 import ctypes
 import os
 import re
+import subprocess
+import sys
 
 import pytest
 
@@ -196,6 +198,17 @@ def test_narrow_path_hook():
         assert pg.set_narrow_path(0) == 0
     finally:
         pg.set_narrow_path(prev)
+
+
+def test_library_loads_after_torch():
+    """The library binds to torch's HIP runtime: loading it imports torch
+    first (a fresh interpreter that touches only a host entry point)."""
+    code = ("import sys, paged_gqa_decode_attn_amd as pg; assert 'torch' not in sys.modules; "
+            "pg.choose_splits(4096, 1, 1, 1); print('torch' in sys.modules)")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, timeout=300,
+                       cwd=os.path.dirname(os.path.dirname(os.path.abspath(__file__))))
+    assert r.returncode == 0, r.stderr[-2000:]
+    assert r.stdout.strip().endswith("True")
 
 
 def test_missing_library_is_loud(tmp_path, monkeypatch):
