@@ -289,7 +289,7 @@ int32_t pgqa_set_merge_wait_ticks(int32_t ticks);
 /*
  * Test hook for the two page steps of narrow tiles (no page defines it).
  * Tiles of at most 4 columns (columns = rows of the tile x heads per kv
- * head) at hd 64 and 128 can run their scores and P.V either on MFMA, in
+ * head) at hd 64, 128 and 256 can run their scores and P.V either on MFMA, in
  * 16-column blocks of which the tile fills at most 4, or on the vector ALU
  * with packed bf16 dot products.  mode 0 (the default) takes the vector-ALU
  * step in launches of more than 512 workgroups and MFMA otherwise; 1 takes

@@ -103,7 +103,7 @@ def counter_capacity() -> int:
 
 def set_narrow_path(mode: int) -> int:
     """Test hook (``pgqa_set_narrow_path``): page step of tiles of at most 4
-    columns at hd 64/128 -- 0 by launch size (default), 1 vector ALU, 2 MFMA;
+    columns at hd 64-256 -- 0 by launch size (default), 1 vector ALU, 2 MFMA;
     returns the previous mode."""
     rc = int(lib().pgqa_set_narrow_path(mode))
     if rc < 0:

@@ -23,6 +23,9 @@
 //   * pgqa_wave_kernel (hd 64 to 256): 16-column tiles, 4 waves each taking
 //     every 4th page of the split with their own softmax state (K straight
 //     from HBM into MFMA operand registers); narrow groups, batched decode.
+//     Its vector-ALU form takes tiles of at most 4 columns in large launches:
+//     packed bf16 dot products and DPP sums instead of mostly empty MFMA
+//     tiles, K and V both straight into registers.
 //   * pgqa_slice_kernel (hd 512, tiles of up to 16 columns): the 4 waves take
 //     every page, each a quarter of hd, with RING pages in flight per wave in
 //     registers; the partial scores are summed through LDS, so all waves hold
@@ -664,7 +667,7 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
 constexpr int kNarrowCols = 4;
 
 // VALU = false: scores and P.V on MFMA, 16-column tiles.
-// VALU = true (hd 64 and 128, tiles of at most kNarrowCols columns): the page
+// VALU = true (hd 64 to 256, tiles of at most kNarrowCols columns): the page
 // step runs on the vector ALU with packed bf16 dot products
 // (v_dot2_f32_bf16), cross-lane sums through DPP, and no LDS staging of V;
 // the wave's state is moved into the MFMA form's output layout at the end,
@@ -752,8 +755,8 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   constexpr int CH = HD / 8;        // 16-byte chunks per token row
   constexpr int TPL = 64 / CH;      // tokens per 64-lane load
   constexpr int NLD = kPage / TPL;  // loads per page, of K and of V
-  static_assert(!VALU || ((HD == 64 || HD == 128) && NLD * kNarrowCols == CH && NLD == VLD),
-                "the vector-ALU form is built for hd 64 and 128");
+  static_assert(!VALU || ((HD == 64 || HD == 128 || HD == 256) && NLD * kNarrowCols == CH && NLD == VLD),
+                "the vector-ALU form is built for hd 64 to 256");
   const int cl = lane % CH, tg = lane / CH;
   const int vc = cl % kNarrowCols;                 // score column of this lane
   const int vtok = TPL * (cl / kNarrowCols) + tg;  // and its token in the page
@@ -850,8 +853,10 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
         part[j * kNarrowCols + c] = sdot;
       }
     }
-    // sum over the CH lanes of a token row: lane bit 3 (hd 128), 2, 1, 0
-    if constexpr (CH == 16) fold_half<kDppRor8, 16>(part, (lane & 8) != 0);
+    // sum over the CH lanes of a token row: lane bit 4 (hd 256), 3 (hd 128 and
+    // 256), 2, 1, 0
+    if constexpr (CH == 32) fold_half_xor<16, 32>(part, (lane & 16) != 0);
+    if constexpr (CH >= 16) fold_half<kDppRor8, 16>(part, (lane & 8) != 0);
     fold_half<kDppHalfMirror, 8>(part, (lane & 4) != 0);
     fold_half<kDppXor2, 4>(part, (lane & 2) != 0);
     fold_half<kDppXor1, 2>(part, (lane & 1) != 0);
@@ -1042,19 +1047,20 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   }
 
   if constexpr (VALU) {
-    // P.V partials: transposing sum over the lanes of one chunk (lane bits
-    // 5, 4, and 3 at hd 64) leaves each lane NKEEP outputs of one column
+    // P.V partials: transposing sum over the lanes of one chunk (lane bit 5;
+    // 4 from hd 128 down; 3 at hd 64) leaves each lane NKEEP outputs
     float fv[kNarrowCols * 8];
 #pragma unroll
     for (int c = 0; c < kNarrowCols; ++c)
 #pragma unroll
       for (int e = 0; e < 8; ++e) fv[c * 8 + e] = vacc[c][e];
     fold_half_xor<32, 32>(fv, (lane & 32) != 0);
-    fold_half_xor<16, 16>(fv, (lane & 16) != 0);
+    if constexpr (CH <= 16) fold_half_xor<16, 16>(fv, (lane & 16) != 0);
     if constexpr (CH == 8) fold_half<kDppRor8, 8>(fv, (lane & 8) != 0);
-    constexpr int NKEEP = CH == 8 ? 4 : 8;
-    const int fcol = ((lane >> 5) & 1) * 2 + ((lane >> 4) & 1);
-    const int fe0 = CH == 8 ? ((lane >> 3) & 1) * 4 : 0;
+    // the lane keeps values v = vbase + i (v = 8 column + element)
+    constexpr int NKEEP = CH / 2;
+    const int vbase = ((lane >> 5) & 1) * 16 + (CH <= 16 ? ((lane >> 4) & 1) * 8 : 0) +
+                      (CH == 8 ? ((lane >> 3) & 1) * 4 : 0);
     // weight sums over each column's 16 lanes
     vl += __shfl_xor(vl, 4);
     vl += __shfl_xor(vl, 8);
@@ -1065,7 +1071,7 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
     float *ob = reinterpret_cast<float *>(vt);
     static_assert((kNarrowCols * HD + 2 * kNarrowCols) * 4 <= kPage * VSTR * 2, "state must fit the V staging area");
 #pragma unroll
-    for (int i = 0; i < NKEEP; ++i) ob[fcol * HD + cl * 8 + fe0 + i] = fv[i];
+    for (int i = 0; i < NKEEP; ++i) ob[((vbase + i) >> 3) * HD + cl * 8 + ((vbase + i) & 7)] = fv[i];
     if (lane < kNarrowCols) {
       ob[kNarrowCols * HD + lane] = vl;
       ob[kNarrowCols * HD + kNarrowCols + lane] = vm;
@@ -2352,7 +2358,7 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
     if (p.kind != 2) return hipErrorInvalidValue;
     hipLaunchKernelGGL(pgqa_slice_kernel<HD>, grid, block, 0, stream, a);
   } else {
-    if constexpr (HD <= 128) {
+    if constexpr (HD <= 256) {
       if (p.valu) {
         hipLaunchKernelGGL((pgqa_wave_kernel<HD, true>), grid, block, 0, stream, a);
         return hipGetLastError();
@@ -2447,14 +2453,15 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
   // Tiles of at most 4 columns (one row of a group of up to 4 heads, or a few
-  // rows of a narrower group) at hd 64 and 128 take the vector-ALU page step
+  // rows of a narrower group) at hd 64 to 256 take the vector-ALU page step
   // in launches of more than kRankMinBlocks workgroups: measured level with
-  // the MFMA step at hd 128 and 4% faster at hd 64 on batched decode, but
+  // the MFMA step at hd 128, 4% faster at hd 64 and 2-10% faster at hd 256
+  // (two waves per SIMD where the MFMA form fits one) on batched decode, but
   // 1.6 us slower on a one-workgroup call, so smaller launches keep MFMA.
   // Rows per tile then drop to 4 / group, so no tile has more columns.
   {
     const int mode = g_narrow_path.load(std::memory_order_relaxed);
-    const bool fits = plan.kind == 0 && (hd == 64 || hd == 128) && group <= kNarrowCols;
+    const bool fits = plan.kind == 0 && (hd == 64 || hd == 128 || hd == 256) && group <= kNarrowCols;
     if (fits && mode != 2 && (mode == 1 || blocks > kRankMinBlocks)) {
       plan.valu = 1;
       plan.rmax = static_cast<int>(kNarrowCols / group);

@@ -1,5 +1,5 @@
 """The two page steps of narrow tiles (at most 4 columns, i.e. rows of the
-tile x heads per kv head, at hd 64 and 128): MFMA in 16-column blocks, and
+tile x heads per kv head, at hd 64 to 256): MFMA in 16-column blocks, and
 the vector-ALU step with packed bf16 dot products and DPP sums.  Each case
 runs with the step forced either way (``set_narrow_path``) and must pass the
 per-(row, head) gate against the f64 oracle, give fused == separate bit for
@@ -36,7 +36,7 @@ def say(*a):
 
 
 def narrow(w):
-    return w.hd in (64, 128) and w.nh // w.nkv <= 4
+    return w.hd in (64, 128, 256) and w.nh // w.nkv <= 4
 
 
 @pytest.fixture(scope="module")
@@ -103,12 +103,16 @@ def test_narrow_random_shapes(counters, path, i):
 
 
 def narrow_workload(name):
-    if name == "B64HD64":  # a 64-sequence batch at hd 64 (the shape where the vector-ALU step is fastest)
+    # 64-sequence batches at hd 64 and at hd 256 (2 heads per kv head)
+    if name == "B64HD64":
         return workloads.batched("B64HD64", nseq=64, lmin=512, lmax=4096, nh=32, nkv=8, hd=64)
+    if name == "B64HD256":
+        return workloads.batched("B64HD256", nseq=64, lmin=512, lmax=4096, nh=16, nkv=8, hd=256)
     return workloads.make(name)
 
 
-@pytest.mark.parametrize("name,splits", [("C1", 1), ("C1", 4), ("C4", 3), ("C4NAN", 3), ("B64HD64", 3)])
+@pytest.mark.parametrize("name,splits", [("C1", 1), ("C1", 4), ("C4", 3), ("C4NAN", 3), ("B64HD64", 3),
+                                         ("B64HD256", 3)])
 def test_narrow_configurations(counters, path, name, splits):
     """Both steps on the named narrow configurations, and the default choice."""
     w = narrow_workload(name)
@@ -122,6 +126,6 @@ def test_narrow_configurations(counters, path, name, splits):
     path(0)
     auto = dw.host(dw.run(splits, counters=None))
     units = w.rows * w.nkv * splits
-    want = VALU if units > 512 and w.nh // w.nkv <= 4 and w.hd in (64, 128) else MFMA
+    want = VALU if units > 512 and narrow(w) else MFMA
     say(f"[gpu] narrow {name}: default step {want} over {units} workgroups")
     assert np.array_equal(auto, outs[want]), f"{name}: the default step is not the expected one"
