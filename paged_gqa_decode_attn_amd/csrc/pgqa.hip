@@ -2282,13 +2282,27 @@ struct Plan {
   int hblocks;  // head blocks per kv head
   int valu = 0; // per-wave kernel with the vector-ALU page step
 };
+// The largest split count pgqa_choose_splits gives a batch of sequences (its
+// bandwidth regime's cap; its latency regime stays at or below it from 4
+// (sequence, kv head) units up).
+constexpr int64_t kBatchMaxSplits = 16;
+
 Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   Plan p;
   const int64_t cols = group <= 64 ? group * (rows < 64 / group ? rows : 64 / group) : 64;
   // groups of 8+ heads: several rows of one sequence fill a 64-column tile
   // (multi-row decode); narrower groups keep the per-wave kernel, whose
-  // 16-column tiles waste nothing when every row has its own sequence
-  p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) ? 1 : 0;
+  // 16-column tiles waste nothing when every row has its own sequence.
+  // The host cannot see whether the rows share a sequence (the origins are
+  // device data).  A batch of one-row sequences on the shared-page kernel
+  // would leave each workgroup walking rmax one-row tiles in turn, each on a
+  // fraction of its columns (measured 1.5-1.6x slower than the per-wave
+  // kernel at 8 heads per kv head), so at hd 128 and 256 several rows take
+  // the shared-page kernel only with more splits than any batch is given: a
+  // one-sequence call over a long span.  Shorter one-sequence spans run on
+  // the per-wave kernel, reading each page once per 16 columns.
+  const bool one_sequence = rows == 1 || hd == 512 || splits > kBatchMaxSplits;
+  p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) && one_sequence ? 1 : 0;
   // hd-512 tiles of up to 16 columns: the hd-sliced kernel
   if (hd == 512 && cols <= 16) p.kind = 2;
   p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
@@ -2554,7 +2568,7 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   // The larger of the two wins.
   auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
   const int64_t s_long = nseq == 1 ? std::min(cdiv(256, units), pages / 8)
-                                   : std::min(std::min(cdiv(1536, units), int64_t(16)), pages / 16);
+                                   : std::min(std::min(cdiv(1536, units), kBatchMaxSplits), pages / 16);
   const int64_t s_short = std::min(cdiv(64, units), pages / 4);
   int64_t s = std::max(s_long, s_short);
   if (s > kMaxSplits) s = kMaxSplits;
