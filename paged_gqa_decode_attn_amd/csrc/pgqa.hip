@@ -2289,20 +2289,23 @@ constexpr int64_t kBatchMaxSplits = 16;
 
 Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   Plan p;
-  const int64_t cols = group <= 64 ? group * (rows < 64 / group ? rows : 64 / group) : 64;
-  // groups of 8+ heads: several rows of one sequence fill a 64-column tile
-  // (multi-row decode); narrower groups keep the per-wave kernel, whose
-  // 16-column tiles waste nothing when every row has its own sequence.
   // The host cannot see whether the rows share a sequence (the origins are
-  // device data).  A batch of one-row sequences on the shared-page kernel
-  // would leave each workgroup walking rmax one-row tiles in turn, each on a
-  // fraction of its columns (measured 1.5-1.6x slower than the per-wave
-  // kernel at 8 heads per kv head), so at hd 128 and 256 several rows take
-  // the shared-page kernel only with more splits than any batch is given: a
-  // one-sequence call over a long span.  Shorter one-sequence spans run on
-  // the per-wave kernel, reading each page once per 16 columns.
-  const bool one_sequence = rows == 1 || hd == 512 || splits > kBatchMaxSplits;
-  p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) && one_sequence ? 1 : 0;
+  // device data).  Tiles are sized for several rows of one sequence only
+  // when the split count is above what any batch is given (a one-sequence
+  // call over a long span), or at hd 512; otherwise for one row per
+  // sequence.  Sized for several rows, a batch of one-row sequences would
+  // leave each shared-page workgroup walking rmax one-row tiles in turn, each
+  // on a fraction of its columns (measured 1.4-1.6x slower at 8 and 16 heads
+  // per kv head).  Shorter one-sequence spans then run as if each row were
+  // its own sequence: more workgroups read each page.
+  const bool one_sequence = hd == 512 || splits > kBatchMaxSplits;
+  const int64_t trows = one_sequence ? rows : 1;
+  const int64_t cols = group <= 64 ? group * (trows < 64 / group ? trows : 64 / group) : 64;
+  // groups of 8+ heads: several rows of one sequence fill a 64-column tile
+  // (multi-row decode), as do groups of more than 16 heads on their own;
+  // narrower groups keep the per-wave kernel, whose 16-column tiles waste
+  // nothing when every row has its own sequence
+  p.kind = hd >= 128 && cols > 16 && (group >= 8 || hd == 512) ? 1 : 0;
   // hd-512 tiles of up to 16 columns: the hd-sliced kernel
   if (hd == 512 && cols <= 16) p.kind = 2;
   p.nsl = p.kind == 1 ? (cols <= 16 ? 4 : cols <= 32 ? 2 : 1) : 1;
