@@ -1009,18 +1009,20 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
     wave_lds_sync();
   };
 
-  // Two register sets (hd <= 256): the next page's K and V are in flight while
-  // the current page is computed; past the window's end its last page is
-  // loaded again (already cached) so every step issues the same loads.  At
-  // hd 512 the registers hold one page only (one wave per SIMD; a second set
-  // would live in accumulation registers, and measured slower).
+  // Two register sets (hd <= 128, and the vector-ALU form up to hd 256): the
+  // next page's K and V are in flight while the current page is computed;
+  // past the window's end its last page is loaded again (already cached) so
+  // every step issues the same loads.  The MFMA form at hd 256 holds one page
+  // (214 VGPRs, two waves per SIMD, against 280 and one wave with two sets:
+  // 4-17% faster on batched and multi-row decode, the same bits); the other
+  // wave of the SIMD covers the load latency.
   for (int w0 = 0; w0 < nk; w0 += 128) {
     const int wn = min(128, nk - w0);
     fetch_window(w0);
     bf16x8 kA[KJ];
     u32x4 vA[VLD];
     load_page(0, kA, vA);
-    if constexpr (HD <= 256) {
+    if constexpr (HD <= 128 || VALU) {
       bf16x8 kB[KJ];
       u32x4 vB[VLD];
       for (int k = 0; k < wn; k += 2) {
