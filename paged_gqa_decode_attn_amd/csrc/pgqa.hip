@@ -2294,13 +2294,13 @@ Plan make_plan(int64_t rows, int64_t group, int64_t hd, int64_t splits) {
   // The host cannot see whether the rows share a sequence (the origins are
   // device data).  Tiles are sized for several rows of one sequence only
   // when the split count is above what any batch is given (a one-sequence
-  // call over a long span), or at hd 512; otherwise for one row per
-  // sequence.  Sized for several rows, a batch of one-row sequences would
-  // leave each shared-page workgroup walking rmax one-row tiles in turn, each
-  // on a fraction of its columns (measured 1.4-1.6x slower at 8 and 16 heads
-  // per kv head).  Shorter one-sequence spans then run as if each row were
-  // its own sequence: more workgroups read each page.
-  const bool one_sequence = hd == 512 || splits > kBatchMaxSplits;
+  // call over a long span); otherwise for one row per sequence.  Sized for
+  // several rows, a batch of one-row sequences would leave each shared-page
+  // workgroup walking rmax one-row tiles in turn, each on a fraction of its
+  // columns (measured 1.4-2x slower at 8 and 16 heads per kv head).
+  // Shorter one-sequence spans then run as if each row were its own
+  // sequence: more workgroups read each page.
+  const bool one_sequence = splits > kBatchMaxSplits;
   const int64_t trows = one_sequence ? rows : 1;
   const int64_t cols = group <= 64 ? group * (trows < 64 / group ? trows : 64 / group) : 64;
   // groups of 8+ heads: several rows of one sequence fill a 64-column tile
