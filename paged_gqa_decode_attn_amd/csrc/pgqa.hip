@@ -2565,15 +2565,17 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   // and on sweeps of further lengths, head layouts and batch sizes:
   //  - long spans are bandwidth-bound.  One sequence: about one workgroup per
   //    CU on the 256 CUs (each workgroup's prologue and epilogue then come
-  //    once), at least 8 pages per split.  A batch: about 6 workgroups per CU
-  //    (with the longest rows dispatched first, uneven lengths still balance),
-  //    at most 16 splits, at least 16 pages per split;
+  //    once), at least 8 pages per split.  A batch: about 4 workgroups per CU
+  //    up to 256 (sequence, kv head) units, 6 above (with the longest rows
+  //    dispatched first, uneven lengths still balance), at most 16 splits, at
+  //    least 16 pages per split;
   //  - short spans are latency-bound: about 64 workgroups in all, at least 4
   //    pages per split.
   // The larger of the two wins.
   auto cdiv = [](int64_t x, int64_t y) { return (x + y - 1) / y; };
+  const int64_t batch_wgs = units <= 256 ? 1024 : 1536;
   const int64_t s_long = nseq == 1 ? std::min(cdiv(256, units), pages / 8)
-                                   : std::min(std::min(cdiv(1536, units), kBatchMaxSplits), pages / 16);
+                                   : std::min(std::min(cdiv(batch_wgs, units), kBatchMaxSplits), pages / 16);
   const int64_t s_short = std::min(cdiv(64, units), pages / 4);
   int64_t s = std::max(s_long, s_short);
   if (s > kMaxSplits) s = kMaxSplits;

@@ -99,7 +99,10 @@ def test_choose_splits_on_the_measured_shapes():
         (32768, 1, 8, 1): 32,      # one row, hd 128, 8 kv heads: 34.8 us against 48.3 at 128
         (16384, 8, 1, 8): 128,     # 8 rows x 8 heads, 16K: 28.4 us against 29.6 at 64
         (16003, 4, 8, 1): 16,      # batch of 4: 37.8 us against 63.0 at 48
-        (16003, 16, 8, 1): 12,     # batch of 16
+        (16384, 8, 8, 1): 16,      # batch of 8: 71.1 / 67.3 us against 72.8 / 70.9 at 12
+        (16384, 16, 8, 1): 8,      # batch of 16: 115.8 / 114.1 us against 121.6 / 117.6 at 12
+        (16384, 32, 8, 1): 4,      # batch of 32: 202.4 / 203.5 us against 206.9 / 205.1 at 6
+        (16384, 32, 32, 1): 2,     # batch of 32, one head per kv head: 729.2 against 737.9 us at 1
     }
     for args, want in cases.items():
         assert pg.choose_splits(*args) == want, (args, pg.choose_splits(*args), want)
