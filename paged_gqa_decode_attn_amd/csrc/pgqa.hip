@@ -666,13 +666,16 @@ __device__ void owned_merge(const DecodeArgs &a, int t0, int kh, int hb, int nro
 // Tiles of at most this many columns may take the vector-ALU page step.
 constexpr int kNarrowCols = 4;
 
+// OWNED: the parallel fused merge is compiled in (hd 256; at hd 128 a form of
+// its own, launched only for merges that use it, since it costs the kernel a
+// wave per SIMD: 192 against 152 VGPRs).
 // VALU = false: scores and P.V on MFMA, 16-column tiles.
 // VALU = true (hd 64 to 256, tiles of at most kNarrowCols columns): the page
 // step runs on the vector ALU with packed bf16 dot products
 // (v_dot2_f32_bf16), cross-lane sums through DPP, and no LDS staging of V;
 // the wave's state is moved into the MFMA form's output layout at the end,
 // so the merges and the epilogue are shared.
-template <int HD, bool VALU = false>
+template <int HD, bool VALU = false, bool OWNED = (HD >= 256)>
 __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   constexpr int KJ = HD / 32;   // QK^T MFMA steps (32 hd elements each)
   constexpr int DJ = HD / 16;   // PV MFMA output blocks (16 hd columns each)
@@ -1166,9 +1169,9 @@ __global__ __launch_bounds__(kThreads) void pgqa_wave_kernel(DecodeArgs a) {
   }
   if (!fused) return;
 
-  // Large merges (hd 256 and 512 only; the host sets spin_ticks for those):
-  // all of the unit's workgroups together.  Otherwise the last one alone.
-  if constexpr (HD >= 256) {
+  // Large merges (OWNED forms only; the host sets spin_ticks for those): all
+  // of the unit's workgroups together.  Otherwise the last one alone.
+  if constexpr (OWNED) {
     if (a.spin_ticks > 0) {
       __syncthreads();  // the V staging area is free for the merge scratch
       owned_merge<HD, kThreads>(a, t0, kh, hb, nrows, ncols, 16, split, st, &s_is_last);
@@ -2383,6 +2386,12 @@ hipError_t launch_decode(const DecodeArgs &a, const Plan &p, int64_t blocks, hip
         return hipGetLastError();
       }
     }
+    if constexpr (HD == 128) {
+      if (a.spin_ticks > 0) {
+        hipLaunchKernelGGL((pgqa_wave_kernel<HD, false, true>), grid, block, 0, stream, a);
+        return hipGetLastError();
+      }
+    }
     hipLaunchKernelGGL(pgqa_wave_kernel<HD>, grid, block, 0, stream, a);
   }
   return hipGetLastError();
@@ -2528,7 +2537,7 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   // kOwnedMergeUnits units, the counter layout of that merge), below that the
   // last one to arrive merges it alone.  Both give the same bits.
   const int wait_ticks = g_merge_wait_ticks.load(std::memory_order_relaxed);
-  a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind != 0 || hd >= 256) &&
+  a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind != 0 || hd >= 256 || (hd == 128 && !plan.valu)) &&
                          rows * nkv * plan.hblocks <= kOwnedMergeUnits &&
                          splits * plan.cap * hd * 4 >= kParallelMergeBytes
                      ? (wait_ticks > 0 ? wait_ticks : kClaimSpinTicks)
