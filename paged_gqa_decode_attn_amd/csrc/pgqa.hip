@@ -2532,10 +2532,11 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   a.rank_rows = plan.kind != 1 && rows > 1 && blocks > kRankMinBlocks;
 
   // The merge of one unit reads splits * cap * hd floats of partials: from
-  // 256 KB up the unit's workgroups merge it together, each its own blocks
-  // (every kernel from hd 256, the shared-page kernel from hd 128; at most
-  // kOwnedMergeUnits units, the counter layout of that merge), below that the
-  // last one to arrive merges it alone.  Both give the same bits.
+  // kParallelMergeBytes up the unit's workgroups merge it together, each its
+  // own blocks (every kernel from hd 256; the shared-page kernel and the
+  // per-wave kernel's MFMA step from hd 128; at most kOwnedMergeUnits units,
+  // the counter layout of that merge), below that the last one to arrive
+  // merges it alone.  Both give the same bits.
   const int wait_ticks = g_merge_wait_ticks.load(std::memory_order_relaxed);
   a.spin_ticks = counters != nullptr && splits > 1 && (plan.kind != 0 || hd >= 256 || (hd == 128 && !plan.valu)) &&
                          rows * nkv * plan.hblocks <= kOwnedMergeUnits &&
