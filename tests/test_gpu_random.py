@@ -25,7 +25,7 @@ import torch  # noqa: E402
 from tests.gates import TOL, per_head  # noqa: E402
 from tests.gpu_util import DeviceWorkload, new_counters  # noqa: E402
 
-N_CASES = 120
+N_CASES = 400
 
 
 def say(*a):
