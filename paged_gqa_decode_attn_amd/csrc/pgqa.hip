@@ -1726,6 +1726,7 @@ template <int HD, int NT, int WB>
 __device__ int merge_blocks(const DecodeArgs &a, int t0, int kh, int hb, int nrows, int nblocks, int cap, int first,
                             int step, int S) {
   constexpr int per_col = HD / (32 * WB);
+  static_assert(per_col >= 1 && HD % (32 * WB) == 0, "a merge block must divide hd");
   constexpr int waves = NT / 64;
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
