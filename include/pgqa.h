@@ -292,12 +292,12 @@ int32_t pgqa_set_merge_wait_ticks(int32_t ticks);
  * head) at hd 64, 128 and 256 can run their scores and P.V either on MFMA, in
  * 16-column blocks of which the tile fills at most 4, or on the vector ALU
  * with packed bf16 dot products.  mode 0 (the default) takes the vector-ALU
- * step in launches of more than 512 workgroups and MFMA otherwise; 1 takes
- * the vector-ALU step wherever it applies; 2 never.  The two steps round
- * differently, so their outputs differ in the last bits; each matches the
- * definition to the same bound.  Applies to the calls enqueued after it, from
- * any thread.  Returns the previous mode, or PGQA_EINVAL for a mode outside
- * 0..2.
+ * step at hd 64 and 128 in launches of more than 512 workgroups and MFMA
+ * otherwise; 1 takes the vector-ALU step wherever it applies (hd 256
+ * included); 2 never.  The two steps round differently, so their outputs
+ * differ in the last bits; each matches the definition to the same bound.
+ * Applies to the calls enqueued after it, from any thread.  Returns the
+ * previous mode, or PGQA_EINVAL for a mode outside 0..2.
  */
 int32_t pgqa_set_narrow_path(int32_t mode);
 

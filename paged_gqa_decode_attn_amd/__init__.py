@@ -103,8 +103,9 @@ def counter_capacity() -> int:
 
 def set_narrow_path(mode: int) -> int:
     """Test hook (``pgqa_set_narrow_path``): page step of tiles of at most 4
-    columns at hd 64-256 -- 0 by launch size (default), 1 vector ALU, 2 MFMA;
-    returns the previous mode."""
+    columns at hd 64-256 -- 0 the library's choice (default: the vector ALU
+    at hd 64 and 128 in launches of more than 512 workgroups), 1 vector ALU,
+    2 MFMA; returns the previous mode."""
     rc = int(lib().pgqa_set_narrow_path(mode))
     if rc < 0:
         raise PgqaError(rc, "mode must be 0, 1 or 2")

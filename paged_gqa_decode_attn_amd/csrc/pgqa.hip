@@ -2482,15 +2482,16 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   if (blocks > INT_MAX || blocks * block_threads > int64_t(UINT32_MAX))
     return fail(PGQA_EINVAL, "grid of %lld workgroups too large", (long long)blocks);
   // Tiles of at most 4 columns (one row of a group of up to 4 heads, or a few
-  // rows of a narrower group) at hd 64 to 256 take the vector-ALU page step
+  // rows of a narrower group) at hd 64 and 128 take the vector-ALU page step
   // in launches of more than kRankMinBlocks workgroups: measured level with
-  // the MFMA step at hd 128, 4% faster at hd 64 and 2-10% faster at hd 256
-  // (two waves per SIMD where the MFMA form fits one) on batched decode, but
-  // 1.6 us slower on a one-workgroup call, so smaller launches keep MFMA.
+  // the MFMA step at hd 128 and 4% faster at hd 64 on batched decode, but
+  // 1.6 us slower on a one-workgroup call, so smaller launches keep MFMA.  At
+  // hd 256 the MFMA form (one register set, two waves per SIMD) is 2-8%
+  // faster, so the vector-ALU form runs there only when forced (mode 1).
   // Rows per tile then drop to 4 / group, so no tile has more columns.
   {
     const int mode = g_narrow_path.load(std::memory_order_relaxed);
-    const bool fits = plan.kind == 0 && (hd == 64 || hd == 128 || hd == 256) && group <= kNarrowCols;
+    const bool fits = plan.kind == 0 && (hd == 64 || hd == 128 || (hd == 256 && mode == 1)) && group <= kNarrowCols;
     if (fits && mode != 2 && (mode == 1 || blocks > kRankMinBlocks)) {
       plan.valu = 1;
       plan.rmax = static_cast<int>(kNarrowCols / group);
