@@ -57,6 +57,22 @@ extern "C" {
 int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t rows_per_seq);
 
 /*
+ * pgqa_choose_splits with the head layout (ours: the page's call passes no
+ * head count, and the best count also depends on which kernel the call
+ * takes).  Same arguments, plus nh (query heads) and hd (head dimension).
+ * Batches (more than one sequence) whose tiles go to the shared-page kernel
+ * -- groups of more than 16 query heads per kv head from hd 128 -- hold one
+ * workgroup per CU, so the count aims at one round of 256 workgroups:
+ * min(floor(256 / units), 16, pages / 16), units = sequences * nkv, at
+ * least the short-span count and 1.  Every other call, and arguments that
+ * attn_decode would refuse (nh not a multiple of nkv, hd outside
+ * {64, 128, 256, 512}), gets pgqa_choose_splits's count.  Returns a count in
+ * [1, PGQA_MAX_SPLITS]; it only affects speed.  Never fails.
+ */
+int32_t pgqa_choose_splits_heads(int64_t kv_span, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
+                                 int64_t rows_per_seq);
+
+/*
  * Bytes of the partial-result buffer attn_decode needs for `splits` splits
  * (span-02 test page, `run()`: the `decode_part_bytes` call).  Formula (ours):
  * rows * nh * splits * (hd + 2) * 4 -- an f32 unnormalised output row plus the

@@ -7,7 +7,8 @@ return.  Every step of the computation runs in the HIP kernels; there is no
 CPU or framework fallback, and a missing library is an error.
 
 Entry points (same names and argument order as the C ABI, after the span-02
-GPU test page's ``attn`` calls): ``choose_splits``, ``decode_part_bytes``,
+GPU test page's ``attn`` calls): ``choose_splits`` (and ``choose_splits_heads``,
+the same count with the head layout), ``decode_part_bytes``,
 ``counter_capacity``, ``attn_decode``, ``prefill_rows_per_tile``,
 ``make_tiles``, ``attn_prefill``; ``qk_rope_prep``, the QK-norm + RoPE step
 that fills the pool before decode; ``attn_decode_noalloc``, decode for
@@ -55,6 +56,8 @@ def lib() -> ctypes.CDLL:
         i64, p = ctypes.c_int64, ctypes.c_void_p
         h.pgqa_choose_splits.restype = ctypes.c_int32
         h.pgqa_choose_splits.argtypes = [i64, i64, i64, i64]
+        h.pgqa_choose_splits_heads.restype = ctypes.c_int32
+        h.pgqa_choose_splits_heads.argtypes = [i64, i64, i64, i64, i64, i64]
         h.pgqa_tile_splits.restype = ctypes.c_int32
         h.pgqa_tile_splits.argtypes = [i64, i64]
         h.pgqa_decode_part_bytes.restype = ctypes.c_uint64
@@ -86,6 +89,10 @@ def lib() -> ctypes.CDLL:
 
 def choose_splits(kv_span: int, rows: int, nkv: int, rows_per_seq: int) -> int:
     return int(lib().pgqa_choose_splits(kv_span, rows, nkv, rows_per_seq))
+
+
+def choose_splits_heads(kv_span: int, rows: int, nh: int, nkv: int, hd: int, rows_per_seq: int) -> int:
+    return int(lib().pgqa_choose_splits_heads(kv_span, rows, nh, nkv, hd, rows_per_seq))
 
 
 def tile_splits(pages: int, splits: int) -> int:

@@ -2595,6 +2595,25 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
   return static_cast<int32_t>(s);
 }
 
+int32_t pgqa_choose_splits_heads(int64_t kv_span, int64_t rows, int64_t nh, int64_t nkv, int64_t hd,
+                                 int64_t rows_per_seq) {
+  const int32_t s = pgqa_choose_splits(kv_span, rows, nkv, rows_per_seq);
+  if (kv_span < 1 || rows < 1 || nkv < 1 || nh < nkv || nh % nkv != 0) return s;
+  if (hd != 64 && hd != 128 && hd != 256 && hd != 512) return s;
+  if (rows_per_seq < 1 || rows_per_seq > rows) rows_per_seq = rows;
+  const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
+  if (nseq == 1 || make_plan(rows, nh / nkv, hd, s).kind != 1) return s;
+  // The shared-page kernel holds one workgroup per CU: a second round of
+  // workgroups costs a whole page loop more (measured over split counts 1..16
+  // on batches of 8..128 sequences with 32 and 64 heads per kv head: the best
+  // count gives about 256 workgroups).
+  const int64_t units = nseq * nkv;
+  const int64_t pages = (kv_span + kPage - 1) / kPage;
+  const int64_t s_round = std::min(std::min(256 / units, kBatchMaxSplits), pages / 16);
+  const int64_t s_short = std::min((64 + units - 1) / units, pages / 4);
+  return static_cast<int32_t>(std::max(std::max(s_round, s_short), int64_t(1)));
+}
+
 int32_t pgqa_tile_splits(int64_t pages, int64_t splits) {
   if (splits < 1) return 1;
   return splits_for_pages(pages, splits < kMaxSplits ? splits : kMaxSplits);

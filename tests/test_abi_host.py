@@ -26,7 +26,7 @@ def test_library_exports_every_declared_symbol():
     assert {"pgqa_attn_decode", "pgqa_choose_splits", "pgqa_decode_part_bytes",
             "pgqa_counter_capacity", "pgqa_last_error", "pgqa_attn_prefill", "pgqa_make_tiles",
             "pgqa_prefill_rows_per_tile", "pgqa_qk_rope_prep", "pgqa_set_merge_wait_ticks",
-            "pgqa_set_narrow_path",
+            "pgqa_set_narrow_path", "pgqa_choose_splits_heads",
             "pgqa_attn_decode_noalloc", "pgqa_tile_splits"} <= set(names)
     h = ctypes.CDLL(pg.LIB_PATH)
     for n in names:
@@ -341,3 +341,32 @@ def test_read_probe_refuses_bad_patterns():
     assert f(buf, 4096, 1, 8, 2, sink, None) == -1       # paired needs two blocks at least
     assert f(buf, 1 << 20, 3, 8, 2, sink, None) == -1    # 256 blocks not divisible by 3 workgroups
     assert f(buf, 1 << 20, 16, 3, 0, sink, None) == -1   # unroll 3 not built
+
+
+def test_choose_splits_heads():
+    """The head-aware count: batches whose tiles take the shared-page kernel
+    (more than 16 query heads per kv head from hd 128) aim at one round of
+    256 workgroups, the counts measured best on batches with lengths 512..16384
+    (separate and fused merge); everything else keeps pgqa_choose_splits's
+    count."""
+    span = 16384
+    for nseq, nh, nkv, hd, want in [(8, 32, 1, 128, 16), (16, 32, 1, 128, 16), (32, 32, 1, 128, 8),
+                                    (64, 32, 1, 128, 4), (128, 32, 1, 128, 2), (32, 32, 1, 256, 8),
+                                    (16, 64, 2, 128, 8), (64, 64, 2, 128, 2), (512, 32, 1, 128, 1)]:
+        assert pg.choose_splits_heads(span, nseq, nh, nkv, hd, 1) == want, (nseq, nh, nkv, hd)
+    # other kernels, one sequence, refused arguments: the plain count
+    for span, rows, nh, nkv, hd, rps in [(16384, 64, 32, 8, 128, 1), (16384, 64, 32, 2, 128, 1),
+                                         (16384, 64, 64, 1, 64, 1), (32768, 1, 16, 2, 512, 1),
+                                         (131072, 8, 8, 1, 256, 8), (131072, 8, 64, 1, 128, 8),
+                                         (4096, 4, 16, 8, 256, 4), (16384, 64, 33, 2, 128, 1),
+                                         (16384, 64, 32, 1, 96, 1)]:
+        assert pg.choose_splits_heads(span, rows, nh, nkv, hd, rps) == pg.choose_splits(span, rows, nkv, rps)
+    # a short span keeps the short-span floor; degenerate input gives 1
+    assert pg.choose_splits_heads(256, 64, 32, 1, 128, 1) == pg.choose_splits(256, 64, 1, 1)
+    assert pg.choose_splits_heads(0, 1, 1, 1, 128, 1) == 1
+    for span in (1, 17, 5000, 1 << 20):
+        for nseq in (2, 3, 300, 5000):
+            s = pg.choose_splits_heads(span, nseq, 48, 1, 256, 1)
+            assert 1 <= s <= 256 and s == pg.choose_splits_heads(span, nseq, 48, 1, 256, 1)
+            if nseq * 16 >= 64:  # no short-span floor above the round's count
+                assert s <= 16

@@ -1,0 +1,57 @@
+"""Batches with more than 16 query heads per kv head, at the split count
+pgqa_choose_splits_heads gives them (one round of the shared-page kernel's
+workgroups): each (row, head) meets the f64 oracle, the fused merge equals
+the separate combine bit for bit, and the counters end at zero.  The
+lengths are spread like the batched workload's (a narrower range keeps the
+oracle quick), so the tiles' split counts differ from row to row."""
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+
+pytestmark = pytest.mark.gpu
+
+from tests.gpu_env import need_gpu  # noqa: E402
+
+need_gpu()
+import torch  # noqa: E402
+
+import paged_gqa_decode_attn_amd as pg  # noqa: E402
+from tests.gates import TOL, per_head  # noqa: E402
+from tests.gpu_util import DeviceWorkload, new_counters  # noqa: E402
+
+SHAPES = [  # nseq, nh, nkv, hd, lmin, lmax
+    (32, 32, 1, 128, 64, 3000),
+    (12, 64, 2, 128, 1, 2500),
+    (20, 32, 1, 256, 300, 2000),
+    (6, 48, 2, 256, 16, 1200),
+    (3, 32, 1, 512, 700, 900),
+]
+
+
+def say(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+@pytest.mark.parametrize("shape", SHAPES, ids=[f"{s[0]}x{s[1]}_{s[2]}_{s[3]}" for s in SHAPES])
+def test_wide_group_batch_at_the_chosen_count(shape):
+    nseq, nh, nkv, hd, lmin, lmax = shape
+    w = workloads.batched(f"wide{nseq}_{nh}_{nkv}_{hd}", nseq=nseq, lmin=lmin, lmax=lmax, nh=nh, nkv=nkv, hd=hd,
+                          len_seed=31 + nseq, data_seed=4000 + hd)
+    span = int(np.max(w.kv_last)) + 1
+    splits = pg.choose_splits_heads(span, w.rows, nh, nkv, hd, 1)
+    say(f"[gpu] wide group {shape}: splits {splits}")
+    assert 1 <= splits <= 256
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    sep = dw.host(dw.run(splits, counters=None))
+    whole, worst, at = per_head(sep, ref)
+    say(f"[gpu] wide group {shape}: rel_rms={whole:.3e} worst {at}: {worst:.3e}")
+    assert worst < TOL, (shape, at, worst)
+    cnt = new_counters()
+    fused = dw.host(dw.run(splits, counters=cnt))
+    assert int(cnt.abs().sum().item()) == 0, "counters not back at zero"
+    assert np.array_equal(fused, sep), "fused merge != separate combine"
