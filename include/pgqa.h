@@ -62,9 +62,10 @@ int32_t pgqa_choose_splits(int64_t kv_span, int64_t rows, int64_t nkv, int64_t r
  * takes).  Same arguments, plus nh (query heads) and hd (head dimension).
  * Batches (more than one sequence) whose tiles go to the shared-page kernel
  * -- groups of more than 16 query heads per kv head from hd 128 -- hold one
- * workgroup per CU, so the count aims at one round of 256 workgroups:
- * min(floor(256 / units), 16, pages / 16), units = sequences * nkv, at
- * least the short-span count and 1.  Every other call, and arguments that
+ * workgroup per CU, so the count aims at W = 256 workgroups (one round)
+ * below 64 units and W = 512 (two rounds, rows taken longest first) from 64:
+ * min(floor(W / units), 16, pages / 16), units = sequences * nkv, at least
+ * the short-span count and 1.  Every other call, and arguments that
  * attn_decode would refuse (nh not a multiple of nkv, hd outside
  * {64, 128, 256, 512}), gets pgqa_choose_splits's count.  Returns a count in
  * [1, PGQA_MAX_SPLITS]; it only affects speed.  Never fails.

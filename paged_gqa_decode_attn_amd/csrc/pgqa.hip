@@ -112,7 +112,7 @@ struct DecodeArgs {
   const int32_t *page_map;
   int rows, nh, nkv, group, window, splits, rmax, hblocks;
   int cap;  // columns per tile: 16 (per-wave kernel) or 16 * column blocks (shared-page kernel)
-  int rank_rows;  // per-wave kernel: take rows longest first (large launches only)
+  int rank_rows;  // take rows longest first (large launches; the shared-page kernel with one-row tiles)
   int spin_ticks;  // fused merge: > 0 selects the parallel (owned-block) merge and bounds each
                    // workgroup's wait for the unit's last arrival (100 MHz ticks)
   // prefill: caller-made tiles (runs of rows on one sequence, at most
@@ -442,6 +442,7 @@ __device__ __forceinline__ int prefill_subtile(const DecodeArgs &a, int p, int &
 // launches and batches of more than kRankRows rows keep their own order.
 constexpr int kRankRows = 1024;
 constexpr int64_t kRankMinBlocks = 512;  // launches this large take rows longest first
+constexpr int64_t kSharedRankMinBlocks = 256;  // ... on the shared-page kernel (one workgroup per CU)
 constexpr int kRankLenMax = (1 << 30) - 1;  // longer rows rank as equals
 __device__ __forceinline__ int row_of_rank(const DecodeArgs &a, int p, int lane) {
   if (!a.rank_rows || a.rows > kRankRows) return p;
@@ -1915,7 +1916,7 @@ __global__ __launch_bounds__(kSharedThreads) void pgqa_shared_kernel(DecodeArgs 
   // (runs of rows on one sequence) one after another
   // (prefill: one caller-made sub-tile)
   int sub_rows = 0;
-  int rb0 = (b / a.nkv) * a.rmax;
+  int rb0 = a.rank_rows ? row_of_rank(a, b / a.nkv, lane) : (b / a.nkv) * a.rmax;  // ranked: one-row blocks
   int rb1 = min(rb0 + a.rmax, a.rows);
   if (a.tile_row0) {
     rb0 = prefill_subtile(a, b / a.nkv, sub_rows);
@@ -2531,7 +2532,11 @@ int decode_call(void *out, void *part, const void *q, const void *k_pool, const 
   // start; it pays only when the launch is larger than what the GPU holds at
   // once (2-3 per-wave workgroups per CU), so that the order of dispatch
   // decides how the launch ends.
-  a.rank_rows = plan.kind != 1 && rows > 1 && blocks > kRankMinBlocks;
+  // Rows longest first where a launch takes more than one round of
+  // workgroups: the per-wave kernel's large launches, and the shared-page
+  // kernel's one-row tiles beyond the 256 workgroups (one per CU) it holds.
+  a.rank_rows = (plan.kind != 1 || plan.rmax == 1) && rows > 1 &&
+                blocks > (plan.kind == 1 ? kSharedRankMinBlocks : kRankMinBlocks);
 
   // The merge of one unit reads splits * cap * hd floats of partials: from
   // kParallelMergeBytes up the unit's workgroups merge it together, each its
@@ -2603,13 +2608,15 @@ int32_t pgqa_choose_splits_heads(int64_t kv_span, int64_t rows, int64_t nh, int6
   if (rows_per_seq < 1 || rows_per_seq > rows) rows_per_seq = rows;
   const int64_t nseq = (rows + rows_per_seq - 1) / rows_per_seq;
   if (nseq == 1 || make_plan(rows, nh / nkv, hd, s).kind != 1) return s;
-  // The shared-page kernel holds one workgroup per CU: a second round of
-  // workgroups costs a whole page loop more (measured over split counts 1..16
-  // on batches of 8..128 sequences with 32 and 64 heads per kv head: the best
-  // count gives about 256 workgroups).
+  // The shared-page kernel holds one workgroup per CU.  Below 64 units one
+  // round of 256 workgroups is best; from 64 units two rounds, whose rows
+  // are taken longest first, balance the uneven lengths better (measured
+  // over split counts 2..16 on batches of 16..128 sequences with 32 and 64
+  // heads per kv head).
   const int64_t units = nseq * nkv;
   const int64_t pages = (kv_span + kPage - 1) / kPage;
-  const int64_t s_round = std::min(std::min(256 / units, kBatchMaxSplits), pages / 16);
+  const int64_t wgs = units < 64 ? 256 : 512;
+  const int64_t s_round = std::min(std::min(wgs / units, kBatchMaxSplits), pages / 16);
   const int64_t s_short = std::min((64 + units - 1) / units, pages / 4);
   return static_cast<int32_t>(std::max(std::max(s_round, s_short), int64_t(1)));
 }

@@ -346,13 +346,14 @@ def test_read_probe_refuses_bad_patterns():
 def test_choose_splits_heads():
     """The head-aware count: batches whose tiles take the shared-page kernel
     (more than 16 query heads per kv head from hd 128) aim at one round of
-    256 workgroups, the counts measured best on batches with lengths 512..16384
-    (separate and fused merge); everything else keeps pgqa_choose_splits's
-    count."""
+    256 workgroups below 64 units and two rounds from 64, the counts measured
+    best on batches with lengths 512..16384 (separate and fused merge);
+    everything else keeps pgqa_choose_splits's count."""
     span = 16384
     for nseq, nh, nkv, hd, want in [(8, 32, 1, 128, 16), (16, 32, 1, 128, 16), (32, 32, 1, 128, 8),
-                                    (64, 32, 1, 128, 4), (128, 32, 1, 128, 2), (32, 32, 1, 256, 8),
-                                    (16, 64, 2, 128, 8), (64, 64, 2, 128, 2), (512, 32, 1, 128, 1)]:
+                                    (64, 32, 1, 128, 8), (128, 32, 1, 128, 4), (32, 32, 1, 256, 8),
+                                    (64, 32, 1, 256, 8), (16, 64, 2, 128, 8), (64, 64, 2, 128, 4),
+                                    (256, 32, 1, 128, 2), (512, 32, 1, 128, 1)]:
         assert pg.choose_splits_heads(span, nseq, nh, nkv, hd, 1) == want, (nseq, nh, nkv, hd)
     # other kernels, one sequence, refused arguments: the plain count
     for span, rows, nh, nkv, hd, rps in [(16384, 64, 32, 8, 128, 1), (16384, 64, 32, 2, 128, 1),

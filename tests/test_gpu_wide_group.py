@@ -3,7 +3,9 @@ pgqa_choose_splits_heads gives them (one round of the shared-page kernel's
 workgroups): each (row, head) meets the f64 oracle, the fused merge equals
 the separate combine bit for bit, and the counters end at zero.  The
 lengths are spread like the batched workload's (a narrower range keeps the
-oracle quick), so the tiles' split counts differ from row to row."""
+oracle quick), so the tiles' split counts differ from row to row; the last
+shapes launch more than the 256 workgroups the device holds at once, which
+takes the rows longest first."""
 import sys
 
 import numpy as np
@@ -29,6 +31,10 @@ SHAPES = [  # nseq, nh, nkv, hd, lmin, lmax
     (20, 32, 1, 256, 300, 2000),
     (6, 48, 2, 256, 16, 1200),
     (3, 32, 1, 512, 700, 900),
+    # launches of more than 256 workgroups: rows taken longest first
+    (64, 32, 1, 128, 16, 3000),
+    (48, 64, 2, 256, 1, 1500),
+    (40, 48, 1, 512, 100, 1100),
 ]
 
 
