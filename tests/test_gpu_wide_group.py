@@ -61,3 +61,39 @@ def test_wide_group_batch_at_the_chosen_count(shape):
     fused = dw.host(dw.run(splits, counters=cnt))
     assert int(cnt.abs().sum().item()) == 0, "counters not back at zero"
     assert np.array_equal(fused, sep), "fused merge != separate combine"
+
+
+N_RANDOM = 32
+
+
+def draw_wide(i):
+    """Random wide-group batch i (a fixed function of i) and its split count;
+    large enough batches launch more than 256 workgroups."""
+    r = np.random.default_rng(7000 + i)
+    hd = int(r.choice([128, 256, 512]))
+    nkv = int(r.choice([1, 2]))
+    group = int(r.choice([24, 32, 48, 64]))
+    nseq = int(r.integers(2, 81))
+    lmin = int(r.integers(1, 400))
+    lmax = lmin + int(r.integers(0, 1800))
+    while nseq > 2 and nseq * lmax * nkv * hd > (24 << 20):
+        nseq -= 1
+    w = workloads.batched(f"widerand{i}", nseq=nseq, lmin=lmin, lmax=lmax, nh=nkv * group, nkv=nkv, hd=hd,
+                          window=int(r.choice([0, 0, 300])), len_seed=800 + i, data_seed=1900 + i)
+    splits = int(r.choice([1, 2, 3, 4, 6, 8, 12, 16]))
+    return w, splits
+
+
+@pytest.mark.parametrize("i", range(N_RANDOM))
+def test_random_wide_group_batch(i):
+    w, splits = draw_wide(i)
+    say(f"[gpu] wide random {i}: rows={w.rows} nh={w.nh} nkv={w.nkv} hd={w.hd} window={w.window} splits={splits}")
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    sep = dw.host(dw.run(splits, counters=None))
+    whole, worst, at = per_head(sep, ref)
+    assert worst < TOL, (i, at, worst)
+    cnt = new_counters()
+    fused = dw.host(dw.run(splits, counters=cnt))
+    assert int(cnt.abs().sum().item()) == 0, f"case {i}: counters not back at zero"
+    assert np.array_equal(fused, sep), f"case {i}: fused merge != separate combine"
