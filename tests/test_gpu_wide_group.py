@@ -97,3 +97,30 @@ def test_random_wide_group_batch(i):
     fused = dw.host(dw.run(splits, counters=cnt))
     assert int(cnt.abs().sum().item()) == 0, f"case {i}: counters not back at zero"
     assert np.array_equal(fused, sep), f"case {i}: fused merge != separate combine"
+
+
+@pytest.mark.parametrize("kind,nh,nkv,hd,splits", [
+    ("batch", 128, 1, 128, 4), ("batch", 96, 1, 256, 6), ("batch", 192, 2, 128, 16), ("batch", 80, 1, 512, 3),
+    ("single", 128, 1, 128, 64), ("single", 96, 1, 256, 33), ("single", 160, 2, 128, 1), ("single", 72, 1, 512, 20),
+    ("batch", 64, 1, 64, 5), ("single", 48, 1, 64, 40),
+])
+def test_groups_wider_than_a_tile(kind, nh, nkv, hd, splits):
+    """More query heads per kv head than one tile holds (several head blocks
+    per row, the last one partial where the group is not a multiple of the
+    tile), in batches and on one multi-row sequence."""
+    if kind == "batch":
+        w = workloads.batched(f"hb_{nh}_{nkv}_{hd}", nseq=9, lmin=30, lmax=1400, nh=nh, nkv=nkv, hd=hd,
+                              len_seed=55 + nh, data_seed=600 + hd)
+    else:
+        w = workloads.single_sequence(f"hb1_{nh}_{nkv}_{hd}", ctx=2100, rows=3, nh=nh, nkv=nkv, hd=hd, window=700,
+                                      seed=91 + nh)
+    say(f"[gpu] wide tile {kind} nh={nh} nkv={nkv} hd={hd} splits={splits}")
+    dw = DeviceWorkload(w)
+    ref = oracle.decode(w)
+    sep = dw.host(dw.run(splits, counters=None))
+    whole, worst, at = per_head(sep, ref)
+    assert worst < TOL, (kind, nh, hd, at, worst)
+    cnt = new_counters()
+    fused = dw.host(dw.run(splits, counters=cnt))
+    assert int(cnt.abs().sum().item()) == 0, "counters not back at zero"
+    assert np.array_equal(fused, sep), "fused merge != separate combine"
